@@ -1,0 +1,16 @@
+"""Muon + AdamW optimizer step for AMD Instinct MI355X (gfx950).
+
+The step runs in hand-written HIP kernels behind the C ABI of
+``include/muon_adamw.h`` (``libmuon_adamw.so``); this package is its Python
+binding. Build the library with ``python -m adamw_optimizer_step_amd.build``.
+"""
+from .api import (  # noqa: F401
+    KELLER_JORDAN, MuonGroup, MuonHParams, adamw_step, bf16_round, momentum_stage,
+    muon_step, muon_workspace_size, muon_workspace_update, newton_schulz, update_stage,
+)
+from ._lib import MuonAdamWError, lib  # noqa: F401
+
+__all__ = [
+    "KELLER_JORDAN", "MuonGroup", "MuonHParams", "MuonAdamWError", "adamw_step", "muon_step",
+    "muon_workspace_size", "muon_workspace_update", "lib",
+]

@@ -1,0 +1,231 @@
+"""Thin Python binding of the Muon + AdamW library.
+
+Argument marshalling only: torch supplies device memory, pointers and the
+current HIP stream; every step of the optimizer runs in the HIP kernels of
+``libmuon_adamw.so``. Names follow the C ABI (include/muon_adamw.h).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Union
+
+import torch
+
+from . import _lib as L
+
+# Keller Jordan's coefficient triple, repeated at every step ("Chapter 4: The
+# MuonAdamW Optimizer", section "Polar Express: Newton-Schulz Orthogonalization").
+KELLER_JORDAN = (3.4445, -4.7750, 2.0315)
+
+_DT = {torch.bfloat16: L.MA_BF16, torch.float32: L.MA_F32}
+_PREC = {"bf16": L.MA_BF16, "f32": L.MA_F32}
+_EQ = {"off": L.MA_EQ_OFF, "pre": L.MA_EQ_ROWS_PRE, "post": L.MA_EQ_ROWS_POST}
+_SCALE = {"none": L.MA_SCALE_NONE, "sqrt_max1_r_over_c": L.MA_SCALE_SQRT_MAX1_R_OVER_C}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)") from None
+
+
+def _stream(device: torch.device, stream=None) -> Optional[int]:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class MuonHParams:
+    lr: float = 0.02
+    momentum: float = 0.95
+    weight_decay: float = 0.0
+    nesterov: bool = True
+    ns_steps: int = 5
+    coeffs: Sequence = KELLER_JORDAN   # one (a, b, c) triple, or ns_steps triples
+    cautious: bool = False
+    equilibrate: str = "off"           # off | pre | post
+    ns_precision: str = "bf16"         # bf16 | f32
+    lr_scale: str = "sqrt_max1_r_over_c"
+    norm_eps: float = 1e-7
+    eq_eps: float = 1e-7
+
+    def table(self) -> List[float]:
+        c = list(self.coeffs)
+        if len(c) == 3 and all(isinstance(v, (int, float)) for v in c):
+            c = [tuple(c)] * self.ns_steps
+        if len(c) != self.ns_steps:
+            raise ValueError("coefficient table length must equal ns_steps")
+        return [float(v) for t in c for v in t]
+
+    def to_c(self):
+        tab = self.table()
+        arr = (C.c_float * max(1, len(tab)))(*tab)
+        hp = L.MuonHParamsC(
+            lr=self.lr, momentum=self.momentum, weight_decay=self.weight_decay,
+            nesterov=int(bool(self.nesterov)), ns_steps=int(self.ns_steps),
+            abc=C.cast(arr, C.POINTER(C.c_float)), cautious=int(bool(self.cautious)),
+            equilibrate=_EQ[self.equilibrate], ns_precision=_PREC[self.ns_precision],
+            lr_scale=_SCALE[self.lr_scale], norm_eps=self.norm_eps, eq_eps=self.eq_eps)
+        return hp, arr
+
+
+def _matrix_ptrs(x: Union[torch.Tensor, Sequence[torch.Tensor]], rows: int, cols: int) -> List[int]:
+    if isinstance(x, torch.Tensor):
+        if x.dim() == 2:
+            x = x.unsqueeze(0)
+        if x.dim() != 3 or tuple(x.shape[1:]) != (rows, cols) or not x.is_contiguous():
+            raise ValueError(f"expected a contiguous [count, {rows}, {cols}] tensor, got {tuple(x.shape)}")
+        step = rows * cols * x.element_size()
+        return [x.data_ptr() + i * step for i in range(x.shape[0])]
+    out = []
+    for t in x:
+        if tuple(t.shape) != (rows, cols) or not t.is_contiguous():
+            raise ValueError(f"expected contiguous ({rows}, {cols}) matrices")
+        out.append(t.data_ptr())
+    return out
+
+
+class MuonGroup:
+    """``count`` same-shape matrices: stacked ``[count, R, C]`` tensors or lists."""
+
+    def __init__(self, params, grads, momentum):
+        first = params if isinstance(params, torch.Tensor) else params[0]
+        self.rows, self.cols = int(first.shape[-2]), int(first.shape[-1])
+        self.device = first.device
+        self.dtypes = tuple(_dt(t if isinstance(t, torch.Tensor) else t[0]) for t in (params, grads, momentum))
+        self.p = _matrix_ptrs(params, self.rows, self.cols)
+        self.g = _matrix_ptrs(grads, self.rows, self.cols)
+        self.m = _matrix_ptrs(momentum, self.rows, self.cols)
+        if not (len(self.p) == len(self.g) == len(self.m)):
+            raise ValueError("params, grads and momentum differ in count")
+        self.count = len(self.p)
+        self._keep = (params, grads, momentum)
+
+    def to_c(self):
+        n = self.count
+        pa, ga, ma = (C.c_void_p * max(1, n))(*self.p), (C.c_void_p * max(1, n))(*self.g), (C.c_void_p * max(1, n))(*self.m)
+        s = L.MuonGroupC(rows=self.rows, cols=self.cols, count=n, param_dtype=self.dtypes[0],
+                         grad_dtype=self.dtypes[1], mom_dtype=self.dtypes[2],
+                         params=C.cast(pa, C.POINTER(C.c_void_p)), grads=C.cast(ga, C.POINTER(C.c_void_p)),
+                         momentum=C.cast(ma, C.POINTER(C.c_void_p)))
+        return s, (pa, ga, ma)
+
+
+def _groups_c(groups: Sequence[MuonGroup]):
+    arr = (L.MuonGroupC * max(1, len(groups)))()
+    keep = []
+    for i, g in enumerate(groups):
+        arr[i], k = g.to_c()
+        keep.append(k)
+    return arr, keep
+
+
+def muon_workspace_size(groups: Sequence[MuonGroup], hp: MuonHParams) -> int:
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    n = L.lib().ma_muon_workspace_size(garr, len(groups), C.byref(h))
+    if n == 0 and groups:
+        L.check(L.MA_ERR_INVALID_ARG)
+    return int(n)
+
+
+def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """One Muon step over ``groups`` (in place). Returns the workspace used."""
+    if not groups:
+        return workspace
+    dev = groups[0].device
+    need = muon_workspace_size(groups, hp)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    L.check(L.lib().ma_muon_step(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
+                                 workspace.numel(), C.c_void_p(_stream(dev, stream))))
+    return workspace
+
+
+def muon_workspace_update(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: torch.Tensor,
+                          group: int, index: int) -> torch.Tensor:
+    """View of the update U of one matrix inside ``workspace`` (parameter layout)."""
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    u, ld, tr, eb = C.c_void_p(), C.c_int64(), C.c_int32(), C.c_int32()
+    L.check(L.lib().ma_muon_workspace_update(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
+                                             group, index, C.byref(u), C.byref(ld), C.byref(tr), C.byref(eb)))
+    g = groups[group]
+    off = u.value - workspace.data_ptr()
+    dt = torch.bfloat16 if eb.value == 2 else torch.float32
+    flat = workspace[off: off + g.rows * ld.value * eb.value].view(dt)
+    return flat.view(g.rows, ld.value)[:, : g.cols]
+
+
+def adamw_step(segments: Sequence[dict], stream=None) -> None:
+    """One AdamW step. Each segment: param, grad, exp_avg, exp_avg_sq (fp32
+    tensors, contiguous), lr, beta1, beta2, eps, weight_decay, step (1-based)."""
+    if not segments:
+        return
+    arr = (L.AdamWSegmentC * len(segments))()
+    dev = segments[0]["param"].device
+    for i, s in enumerate(segments):
+        p, g, m, v = s["param"], s["grad"], s["exp_avg"], s["exp_avg_sq"]
+        for t in (p, g, m, v):
+            if not t.is_contiguous() or t.numel() != p.numel():
+                raise ValueError("AdamW buffers must be contiguous and of equal size")
+        arr[i] = L.AdamWSegmentC(param=p.data_ptr(), grad=g.data_ptr(), exp_avg=m.data_ptr(),
+                                 exp_avg_sq=v.data_ptr(), n=p.numel(), param_dtype=_dt(p),
+                                 grad_dtype=_dt(g), lr=s["lr"], beta1=s.get("beta1", 0.9),
+                                 beta2=s.get("beta2", 0.95), eps=s.get("eps", 1e-8),
+                                 weight_decay=s.get("weight_decay", 0.0), step=int(s["step"]))
+    L.check(L.lib().ma_adamw_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
+
+
+# ---------------------------------------------------------------------------
+# stage entry points (used by the tests)
+# ---------------------------------------------------------------------------
+
+def bf16_round(x: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty(x.numel(), dtype=torch.int16, device=x.device)
+    L.check(L.lib().ma_test_bf16_round(C.c_void_p(x.data_ptr()), C.c_void_p(out.data_ptr()), x.numel(),
+                                       C.c_void_p(_stream(x.device, stream))))
+    return out
+
+
+def momentum_stage(group: MuonGroup, beta: float, nesterov: bool, stream=None) -> torch.Tensor:
+    mt = torch.empty((group.count, group.rows, group.cols), dtype=torch.float32, device=group.device)
+    s, keep = group.to_c()
+    L.check(L.lib().ma_test_muon_momentum(C.byref(s), beta, int(nesterov), C.c_void_p(mt.data_ptr()),
+                                          C.c_void_p(_stream(group.device, stream))))
+    return mt
+
+
+def update_stage(group: MuonGroup, u: torch.Tensor, c_lr: float, c_wd: float, cautious: bool, decay: bool,
+                 stream=None) -> None:
+    if not u.is_contiguous():
+        raise ValueError("u must be contiguous")
+    s, keep = group.to_c()
+    L.check(L.lib().ma_test_muon_update(C.byref(s), C.c_void_p(u.data_ptr()), _dt(u), c_lr, c_wd,
+                                        int(cautious), int(decay), C.c_void_p(_stream(group.device, stream))))
+
+
+def newton_schulz(x0: torch.Tensor, coeffs, ns_steps: int, stream=None) -> torch.Tensor:
+    """Newton-Schulz iteration alone on ``[count, m, n]`` (m <= n), dtype bf16 or fp32."""
+    if x0.dim() == 2:
+        x0 = x0.unsqueeze(0)
+    x0 = x0.contiguous()
+    count, m, n = x0.shape
+    prec = _dt(x0)
+    tab = MuonHParams(ns_steps=ns_steps, coeffs=coeffs).table()
+    arr = (C.c_float * max(1, len(tab)))(*tab)
+    need = L.lib().ma_test_ns_workspace_size(m, n, count, prec)
+    if need == 0 and count > 0:
+        L.check(L.MA_ERR_INVALID_ARG)
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device=x0.device)
+    u = torch.empty_like(x0)
+    L.check(L.lib().ma_test_ns(m, n, count, prec, C.c_void_p(x0.data_ptr()), C.c_void_p(u.data_ptr()),
+                               C.cast(arr, C.POINTER(C.c_float)), ns_steps, C.c_void_p(ws.data_ptr()),
+                               ws.numel(), C.c_void_p(_stream(x0.device, stream))))
+    return u

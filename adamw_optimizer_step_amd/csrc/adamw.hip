@@ -1,0 +1,88 @@
+// AdamW step over many flat fp32 buffers in one launch (gfx950).
+//
+// Rule ("3.9 Optimizers: SGD, Adam, Adafactor, Lion, Muon & Shampoo",
+// section "Implementing AdamW from scratch"; "Chapter 4: The MuonAdamW
+// Optimizer", section "The AdamW Step"), per element, binary32, one rounding
+// per operation, no contraction (built with -ffp-contract=off):
+//     p = p * cd                         (cd = 1 - lr*wd, only when wd != 0)
+//     m = b1*m + c1*g                    (c1 = 1 - b1)
+//     v = b2*v + c2*(g*g)                (c2 = 1 - b2)
+//     p = p - ss * (m / (sqrt(v)/s2 + eps))
+// with ss = lr/(1 - b1^t) and s2 = sqrt(1 - b2^t) formed on the host in fp64.
+//
+// 28 bytes of HBM traffic per element (p, g, m, v read; p, m, v written).
+// Each block streams 4096 consecutive elements of one segment with 16-byte
+// loads (all loads of a thread issued before its arithmetic); a table of
+// segments in the kernel arguments lets one launch cover every buffer, the
+// multi-tensor ("fused"/"foreach") form the pages mention.
+#include "adamw.hpp"
+
+namespace ma {
+
+__device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v, const AdamSeg& S) {
+  if (S.decay) p = __fmul_rn(p, S.cd);
+  m = __fadd_rn(__fmul_rn(S.b1, m), __fmul_rn(S.c1, g));
+  v = __fadd_rn(__fmul_rn(S.b2, v), __fmul_rn(S.c2, __fmul_rn(g, g)));
+  const float den = __fadd_rn(__fdiv_rn(__builtin_sqrtf(v), S.s2), S.eps);
+  p = __fsub_rn(p, __fmul_rn(S.ss, __fdiv_rn(m, den)));
+}
+
+__global__ void __launch_bounds__(256) k_adamw(const AdamArgs a) {
+  const int64_t b = blockIdx.x;
+  int si = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxAdamSegs; ++q)
+    if (q < a.nseg && b >= a.s[q].block_begin) si = q;
+  const AdamSeg& S = a.s[si];
+  const int64_t e0 = (b - S.block_begin) * kAdamBlockElems;
+  const int tid = threadIdx.x;
+  if (S.vec) {
+    constexpr int U = kAdamBlockElems / (256 * 4);
+    float4 p[U], g[U], m[U], v[U];
+    bool full[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = e0 + (int64_t)(u * 256 + tid) * 4;
+      full[u] = i + 4 <= S.n;
+      if (full[u]) {
+        p[u] = *reinterpret_cast<const float4*>(S.p + i);
+        g[u] = *reinterpret_cast<const float4*>(S.g + i);
+        m[u] = *reinterpret_cast<const float4*>(S.m + i);
+        v[u] = *reinterpret_cast<const float4*>(S.v + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = e0 + (int64_t)(u * 256 + tid) * 4;
+      if (full[u]) {
+        adamw_elem(p[u].x, g[u].x, m[u].x, v[u].x, S);
+        adamw_elem(p[u].y, g[u].y, m[u].y, v[u].y, S);
+        adamw_elem(p[u].z, g[u].z, m[u].z, v[u].z, S);
+        adamw_elem(p[u].w, g[u].w, m[u].w, v[u].w, S);
+        *reinterpret_cast<float4*>(S.p + i) = p[u];
+        *reinterpret_cast<float4*>(S.m + i) = m[u];
+        *reinterpret_cast<float4*>(S.v + i) = v[u];
+      } else {
+        for (int64_t j = i; j < S.n && j < i + 4; ++j) {
+          float pp = S.p[j], mm = S.m[j], vv = S.v[j];
+          adamw_elem(pp, S.g[j], mm, vv, S);
+          S.p[j] = pp; S.m[j] = mm; S.v[j] = vv;
+        }
+      }
+    }
+  } else {
+    for (int64_t j = e0 + tid; j < S.n && j < e0 + kAdamBlockElems; j += 256) {
+      float pp = S.p[j], mm = S.m[j], vv = S.v[j];
+      adamw_elem(pp, S.g[j], mm, vv, S);
+      S.p[j] = pp; S.m[j] = mm; S.v[j] = vv;
+    }
+  }
+}
+
+hipError_t launch_adamw(const AdamArgs& a, hipStream_t s) {
+  if (a.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_adamw, dim3((unsigned)a.total_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ma

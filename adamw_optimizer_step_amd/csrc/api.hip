@@ -1,0 +1,695 @@
+// C ABI of the Muon + AdamW library: argument validation, the host plan
+// (orientation, padding, fp64 scalars, workspace carving) and the launch
+// order. See include/muon_adamw.h for the contract of every entry point.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/muon_adamw.h"
+#include "adamw.hpp"
+#include "muon_elem.hpp"
+#include "ns_gemm.hpp"
+
+using namespace ma;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ----------------------------------------------------------------------------
+// kernel timing (ma_profile_*)
+// ----------------------------------------------------------------------------
+struct Profiler {
+  bool active = false;
+  int used = 0;
+  std::vector<hipEvent_t> ev;   // 2 per launch
+  std::vector<int> kind;        // per launch
+} g_prof;
+
+struct ProfScope {
+  int slot = -1;
+  hipStream_t s;
+  ProfScope(int k, hipStream_t st) : s(st) {
+    if (g_prof.active && g_prof.used < (int)g_prof.kind.size()) {
+      slot = g_prof.used++;
+      g_prof.kind[slot] = k;
+      (void)hipEventRecord(g_prof.ev[2 * slot], s);
+    }
+  }
+  ~ProfScope() {
+    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+  }
+};
+
+inline int64_t dt_bytes(int dt) { return dt == MA_BF16 ? 2 : 4; }
+inline bool dt_valid(int dt) { return dt == MA_F32 || dt == MA_BF16; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr NsTile kTileBf16 = {128, 128, 64};
+constexpr NsTile kTileF32 = {128, 128, 32};
+
+// ----------------------------------------------------------------------------
+// plan of one Muon call
+// ----------------------------------------------------------------------------
+struct GroupPlan {
+  int64_t R, C, m, n, m_pad, n_pad, r_ext, c_ext;
+  bool tall;                 // R > C: the iteration runs on X0^T
+  int count;
+  int dt_p, dt_g, dt_m, dt_x;
+  float c_lr, c_wd;
+  int64_t x_stride, a_stride, row_stride;   // elements / floats
+  size_t off_x[2], off_xt[2], off_a, off_b, off_rowsq, off_rowf;   // bytes
+  const ma_muon_group* src;
+  // views in the parameter's layout ("direct") and transposed
+  size_t off_direct(int buf) const { return tall ? off_xt[buf] : off_x[buf]; }
+  size_t off_trans(int buf) const { return tall ? off_x[buf] : off_xt[buf]; }
+  int64_t ld_direct() const { return tall ? m_pad : n_pad; }
+  int64_t ld_trans() const { return tall ? n_pad : m_pad; }
+};
+
+struct Plan {
+  std::vector<GroupPlan> g;
+  size_t bytes = 0;
+};
+
+void plan_group(GroupPlan& p, int64_t R, int64_t C, int count, int dt_x, size_t& off) {
+  p.R = R;
+  p.C = C;
+  p.count = count;
+  p.tall = R > C;
+  p.m = std::min(R, C);
+  p.n = std::max(R, C);
+  p.m_pad = round_up(p.m, kPad);
+  p.n_pad = round_up(p.n, kPad);
+  p.r_ext = p.tall ? p.n_pad : p.m_pad;
+  p.c_ext = p.tall ? p.m_pad : p.n_pad;
+  p.dt_x = dt_x;
+  const int64_t e = dt_bytes(dt_x);
+  p.x_stride = p.m_pad * p.n_pad;
+  p.a_stride = p.m_pad * p.m_pad;
+  p.row_stride = round_up(R, 64);
+  for (int b = 0; b < 2; ++b) {
+    p.off_x[b] = off;  off = align_up(off + (size_t)(count * p.x_stride * e), MA_WORKSPACE_ALIGN);
+    p.off_xt[b] = off; off = align_up(off + (size_t)(count * p.x_stride * e), MA_WORKSPACE_ALIGN);
+  }
+  p.off_a = off;     off = align_up(off + (size_t)(count * p.a_stride * e), MA_WORKSPACE_ALIGN);
+  p.off_b = off;     off = align_up(off + (size_t)(count * p.a_stride * e), MA_WORKSPACE_ALIGN);
+  p.off_rowsq = off; off = align_up(off + (size_t)(count * p.row_stride * 4), MA_WORKSPACE_ALIGN);
+  p.off_rowf = off;  off = align_up(off + (size_t)(count * p.row_stride * 4), MA_WORKSPACE_ALIGN);
+}
+
+int validate_hparams(const ma_muon_hparams* hp) {
+  if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is null");
+  if (hp->ns_steps < 0 || hp->ns_steps > MA_MAX_NS_STEPS)
+    return fail(MA_ERR_INVALID_ARG, "ns_steps %d outside 0..%d", hp->ns_steps, MA_MAX_NS_STEPS);
+  if (hp->ns_steps > 0 && !hp->abc) return fail(MA_ERR_INVALID_ARG, "abc is null with ns_steps > 0");
+  if (hp->equilibrate < MA_EQ_OFF || hp->equilibrate > MA_EQ_ROWS_POST)
+    return fail(MA_ERR_INVALID_ARG, "equilibrate %d is not an ma_eq value", hp->equilibrate);
+  if (hp->lr_scale != MA_SCALE_NONE && hp->lr_scale != MA_SCALE_SQRT_MAX1_R_OVER_C)
+    return fail(MA_ERR_INVALID_ARG, "lr_scale %d is not an ma_scale value", hp->lr_scale);
+  if (!dt_valid(hp->ns_precision)) return fail(MA_ERR_UNSUPPORTED, "ns_precision %d", hp->ns_precision);
+  if (!std::isfinite(hp->lr) || !std::isfinite(hp->momentum) || !std::isfinite(hp->weight_decay) ||
+      !std::isfinite(hp->norm_eps) || !std::isfinite(hp->eq_eps))
+    return fail(MA_ERR_INVALID_ARG, "non-finite hyperparameter");
+  for (int i = 0; i < 3 * hp->ns_steps; ++i)
+    if (!std::isfinite(hp->abc[i])) return fail(MA_ERR_INVALID_ARG, "non-finite coefficient abc[%d]", i);
+  return MA_OK;
+}
+
+struct Range { uintptr_t lo, hi; int tag; };
+
+int check_overlaps(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < rs.size(); ++i)
+    if (rs[i].lo < rs[i - 1].hi)
+      return fail(MA_ERR_INVALID_ARG, "device buffers overlap (%s and %s)",
+                  rs[i - 1].tag == 3 ? "workspace" : "a parameter/gradient/momentum buffer",
+                  rs[i].tag == 3 ? "workspace" : "a parameter/gradient/momentum buffer");
+  return MA_OK;
+}
+
+int validate_group(const ma_muon_group& g, int idx, bool need_ptrs) {
+  if (g.rows <= 0 || g.cols <= 0 || g.count < 0)
+    return fail(MA_ERR_INVALID_ARG, "group %d: rows/cols must be > 0 and count >= 0", idx);
+  if (g.rows > (1 << 24) || g.cols > (1 << 24) || g.rows * g.cols > (int64_t)1 << 31)
+    return fail(MA_ERR_INVALID_ARG, "group %d: matrix too large", idx);
+  if (!dt_valid(g.param_dtype) || !dt_valid(g.grad_dtype) || !dt_valid(g.mom_dtype))
+    return fail(MA_ERR_UNSUPPORTED, "group %d: dtype must be MA_F32 or MA_BF16", idx);
+  if (need_ptrs && g.count > 0) {
+    if (!g.params || !g.grads || !g.momentum)
+      return fail(MA_ERR_INVALID_ARG, "group %d: pointer array is null", idx);
+    for (int i = 0; i < g.count; ++i) {
+      if (!g.params[i] || !g.grads[i] || !g.momentum[i])
+        return fail(MA_ERR_INVALID_ARG, "group %d matrix %d: null device pointer", idx, i);
+      if (((uintptr_t)g.params[i] % dt_bytes(g.param_dtype)) || ((uintptr_t)g.grads[i] % dt_bytes(g.grad_dtype)) ||
+          ((uintptr_t)g.momentum[i] % dt_bytes(g.mom_dtype)))
+        return fail(MA_ERR_INVALID_ARG, "group %d matrix %d: pointer not aligned to its element size", idx, i);
+    }
+  }
+  return MA_OK;
+}
+
+int build_plan(const ma_muon_group* groups, int32_t n, const ma_muon_hparams* hp, Plan& plan,
+               bool need_ptrs) {
+  if (n < 0 || (n > 0 && !groups)) return fail(MA_ERR_INVALID_ARG, "groups is null or n_groups < 0");
+  int rc = validate_hparams(hp);
+  if (rc) return rc;
+  plan.g.clear();
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    rc = validate_group(groups[i], i, need_ptrs);
+    if (rc) return rc;
+    GroupPlan p{};
+    plan_group(p, groups[i].rows, groups[i].cols, groups[i].count, hp->ns_precision, off);
+    p.dt_p = groups[i].param_dtype;
+    p.dt_g = groups[i].grad_dtype;
+    p.dt_m = groups[i].mom_dtype;
+    const double mult = hp->lr_scale == MA_SCALE_SQRT_MAX1_R_OVER_C
+                            ? std::sqrt(std::max(1.0, (double)p.R / (double)p.C)) : 1.0;
+    const double lr_eff = (double)hp->lr * mult;
+    p.c_lr = (float)lr_eff;
+    p.c_wd = (float)(lr_eff * (double)hp->weight_decay);
+    p.src = &groups[i];
+    plan.g.push_back(p);
+  }
+  plan.bytes = off;
+  return MA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char* ws, int first,
+                   int cnt) {
+  ElemArgs a{};
+  a.R = (int32_t)p.R;
+  a.C = (int32_t)p.C;
+  a.count = cnt;
+  a.r_ext = (int32_t)p.r_ext;
+  a.c_ext = (int32_t)p.c_ext;
+  a.tiles_r = (int32_t)(p.r_ext / 64);
+  a.tiles_c = (int32_t)(p.c_ext / 64);
+  const int64_t e = dt_bytes(p.dt_x);
+  a.x_stride = p.x_stride;
+  a.xd = ws + p.off_direct(0) + (size_t)(first * p.x_stride * e);
+  a.xt = ws + p.off_trans(0) + (size_t)(first * p.x_stride * e);
+  a.ld_d = p.ld_direct();
+  a.ld_t = p.ld_trans();
+  a.row_stride = p.row_stride;
+  a.rowsq = reinterpret_cast<float*>(ws + p.off_rowsq) + first * p.row_stride;
+  a.rowf = reinterpret_cast<float*>(ws + p.off_rowf) + first * p.row_stride;
+  a.beta = hp->momentum;
+  a.nesterov = hp->nesterov ? 1 : 0;
+  a.c_lr = p.c_lr;
+  a.c_wd = p.c_wd;
+  a.cautious = hp->cautious ? 1 : 0;
+  a.decay = hp->weight_decay != 0.0f ? 1 : 0;
+  a.norm_eps = hp->norm_eps;
+  a.eq_eps = hp->eq_eps;
+  a.finalize_mode = hp->equilibrate == MA_EQ_ROWS_PRE ? 1 : 0;
+  bool vec = (p.C % 8) == 0;
+  for (int i = 0; i < cnt; ++i) {
+    const int k = first + i;
+    a.mat[i].g = p.src ? p.src->grads[k] : nullptr;
+    a.mat[i].m = p.src ? p.src->momentum[k] : nullptr;
+    a.mat[i].w = p.src ? p.src->params[k] : nullptr;
+    if (p.src) vec = vec && aligned16(a.mat[i].g) && aligned16(a.mat[i].m) && aligned16(a.mat[i].w);
+  }
+  a.vec = vec ? 1 : 0;
+  return a;
+}
+
+// Enqueue T quintic steps for every group of the plan; X[0]/X^T[0] hold X0.
+int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
+               hipStream_t s) {
+  if (T == 0 || plan.g.empty()) return MA_OK;
+  const NsTile tile = dtype == MA_BF16 ? kTileBf16 : kTileF32;
+  // groups with the most work per tile first (they set the tail of a launch)
+  std::vector<int> order;
+  for (int i = 0; i < (int)plan.g.size(); ++i)
+    if (plan.g[i].count > 0) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return plan.g[a].n_pad > plan.g[b].n_pad; });
+  const int64_t e = dt_bytes(dtype);
+  for (int step = 0; step < T; ++step) {
+    const int cur = step & 1, nxt = cur ^ 1;
+    const bool last = step == T - 1;
+    for (int epi = EPI_GRAM; epi <= EPI_AXPY; ++epi) {
+      for (size_t base = 0; base < order.size(); base += kMaxNsGroups) {
+        NsArgs A{};
+        A.a = abc[3 * step];
+        A.b = abc[3 * step + 1];
+        A.c = abc[3 * step + 2];
+        int jobs = 0;
+        const size_t nb = std::min(order.size() - base, (size_t)kMaxNsGroups);
+        for (size_t q = 0; q < nb; ++q) {
+          const GroupPlan& p = plan.g[order[base + q]];
+          NsGroup& G = A.g[q];
+          const int tm = (int)(p.m_pad / tile.bm);
+          const int tn = (int)(p.n_pad / tile.bn);
+          G.count = p.count;
+          G.block_begin = jobs;
+          if (epi == EPI_GRAM || epi == EPI_POLY) {
+            const unsigned char* src = ws + (epi == EPI_GRAM ? p.off_x[cur] : p.off_a);
+            G.P = G.Q = src;
+            G.sP = G.sQ = epi == EPI_GRAM ? p.x_stride : p.a_stride;
+            G.ldP = G.ldQ = (int32_t)(epi == EPI_GRAM ? p.n_pad : p.m_pad);
+            G.K = (int32_t)(epi == EPI_GRAM ? p.n_pad : p.m_pad);
+            G.E = ws + p.off_a;
+            G.sE = p.a_stride;
+            G.ldE = (int32_t)p.m_pad;
+            void* out = ws + (epi == EPI_GRAM ? p.off_a : p.off_b);
+            G.outN = G.outT = out;
+            G.sN = G.sT = p.a_stride;
+            G.ldN = G.ldT = (int32_t)p.m_pad;
+            G.tm = G.tn = tm;
+            G.tiles = tm * (tm + 1) / 2;
+            G.symmetric = 1;
+          } else {
+            G.P = ws + p.off_b;
+            G.sP = p.a_stride;
+            G.ldP = (int32_t)p.m_pad;
+            G.Q = ws + p.off_xt[cur];
+            G.sQ = p.x_stride;
+            G.ldQ = (int32_t)p.m_pad;
+            G.K = (int32_t)p.m_pad;
+            G.E = ws + p.off_xt[cur];
+            G.sE = p.x_stride;
+            G.ldE = (int32_t)p.m_pad;
+            // the last step writes only the copy in the parameter's layout
+            G.outN = (!last || !p.tall) ? (void*)(ws + p.off_x[nxt]) : nullptr;
+            G.outT = (!last || p.tall) ? (void*)(ws + p.off_xt[nxt]) : nullptr;
+            G.sN = G.sT = p.x_stride;
+            G.ldN = (int32_t)p.n_pad;
+            G.ldT = (int32_t)p.m_pad;
+            G.tm = tm;
+            G.tn = tn;
+            G.tiles = tm * tn;
+            G.symmetric = 0;
+          }
+          jobs += G.count * G.tiles;
+        }
+        (void)e;
+        A.n_groups = (int32_t)nb;
+        A.total_jobs = jobs;
+        A.padded_blocks = (jobs + 7) / 8 * 8;
+        hipError_t err;
+        {
+          ProfScope ps(MA_K_GRAM + epi, s);
+          err = launch_ns_gemm(dtype, epi, tile, A, s);
+        }
+        if (err != hipSuccess) return hip_fail(err, "Newton-Schulz GEMM launch");
+      }
+    }
+  }
+  return MA_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+const char* ma_version(void) { return "muon_adamw 0.1 (gfx950)"; }
+
+const char* ma_status_string(int status) {
+  switch (status) {
+    case MA_OK: return "ok";
+    case MA_ERR_INVALID_ARG: return "invalid argument";
+    case MA_ERR_UNSUPPORTED: return "unsupported dtype combination";
+    case MA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ma_last_error(void) { return g_last_error.c_str(); }
+
+int ma_profile_begin(int32_t max_launches) {
+  if (max_launches < 0 || max_launches > (1 << 20)) return fail(MA_ERR_INVALID_ARG, "max_launches out of range");
+  const size_t need = 2 * (size_t)max_launches;
+  while (g_prof.ev.size() < need) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    g_prof.ev.push_back(e);
+  }
+  g_prof.kind.assign(max_launches, -1);
+  g_prof.used = 0;
+  g_prof.active = true;
+  return MA_OK;
+}
+
+int ma_profile_end(void) {
+  g_prof.active = false;
+  return MA_OK;
+}
+
+int ma_profile_read(int32_t kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= MA_K_COUNT || !total_ms || !launches) return fail(MA_ERR_INVALID_ARG, "bad kind or null output");
+  double t = 0.0;
+  int64_t n = 0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    if (g_prof.kind[i] != kind) continue;
+    hipError_t err = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+    t += ms;
+    ++n;
+  }
+  *total_ms = t;
+  *launches = n;
+  return MA_OK;
+}
+
+size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp) {
+  Plan plan;
+  if (build_plan(groups, n_groups, hp, plan, false) != MA_OK) return 0;
+  return plan.bytes;
+}
+
+int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  Plan plan;
+  int rc = build_plan(groups, n_groups, hp, plan, true);
+  if (rc) return rc;
+  if (plan.bytes > 0) {
+    if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is null");
+    if ((uintptr_t)workspace % MA_WORKSPACE_ALIGN)
+      return fail(MA_ERR_WORKSPACE, "workspace is not %d-byte aligned", MA_WORKSPACE_ALIGN);
+    if (workspace_bytes < plan.bytes)
+      return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.bytes);
+  }
+  // no two buffers may overlap (including the workspace)
+  std::vector<Range> rs;
+  for (const GroupPlan& p : plan.g) {
+    const ma_muon_group& g = *p.src;
+    const uintptr_t ne = (uintptr_t)(p.R * p.C);
+    for (int i = 0; i < g.count; ++i) {
+      rs.push_back({(uintptr_t)g.params[i], (uintptr_t)g.params[i] + ne * dt_bytes(p.dt_p), 0});
+      rs.push_back({(uintptr_t)g.grads[i], (uintptr_t)g.grads[i] + ne * dt_bytes(p.dt_g), 1});
+      rs.push_back({(uintptr_t)g.momentum[i], (uintptr_t)g.momentum[i] + ne * dt_bytes(p.dt_m), 2});
+    }
+  }
+  if (plan.bytes > 0) rs.push_back({(uintptr_t)workspace, (uintptr_t)workspace + plan.bytes, 3});
+  rc = check_overlaps(rs);
+  if (rc) return rc;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  hipError_t err;
+  // 1. norms, 2. factors, 3. momentum update and X0 (both layouts)
+  for (const GroupPlan& p : plan.g) {
+    for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
+      const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
+      ElemArgs a = elem_args(p, hp, ws, first, cnt);
+      { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_momentum(p.dt_g, p.dt_m, a, s); }
+      if (err != hipSuccess) return hip_fail(err, "row norms");
+      { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
+      if (err != hipSuccess) return hip_fail(err, "norm finalize");
+      { ProfScope ps(MA_K_PRE, s); err = launch_pre(p.dt_g, p.dt_m, p.dt_x, a, s); }
+      if (err != hipSuccess) return hip_fail(err, "momentum/X0");
+    }
+  }
+  // 4. T quintic steps
+  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s);
+  if (rc) return rc;
+  // 5. (MuonEq POST) and the update
+  const int ub = hp->ns_steps & 1;
+  for (const GroupPlan& p : plan.g) {
+    for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
+      const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
+      ElemArgs a = elem_args(p, hp, ws, first, cnt);
+      a.xd = ws + p.off_direct(ub) + (size_t)(first * p.x_stride * dt_bytes(p.dt_x));
+      a.xt = nullptr;
+      if (hp->equilibrate == MA_EQ_ROWS_POST) {
+        a.finalize_mode = 2;
+        { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_buffer(p.dt_x, a, s); }
+        if (err != hipSuccess) return hip_fail(err, "update row norms");
+        { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
+        if (err != hipSuccess) return hip_fail(err, "update row factors");
+      } else {
+        a.rowf = nullptr;
+      }
+      a.tiles_r = (int32_t)((p.R + 63) / 64);
+      a.tiles_c = (int32_t)((p.C + 63) / 64);
+      { ProfScope ps(MA_K_POST, s); err = launch_post(p.dt_p, p.dt_x, a, s); }
+      if (err != hipSuccess) return hip_fail(err, "update");
+    }
+  }
+  return MA_OK;
+}
+
+int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                             void* workspace, int32_t group, int32_t index, void** u, int64_t* ld,
+                             int32_t* transposed, int32_t* elem_bytes) {
+  Plan plan;
+  int rc = build_plan(groups, n_groups, hp, plan, false);
+  if (rc) return rc;
+  if (!workspace || !u || !ld || !elem_bytes) return fail(MA_ERR_INVALID_ARG, "null output pointer");
+  if (group < 0 || group >= n_groups) return fail(MA_ERR_INVALID_ARG, "group %d out of range", group);
+  const GroupPlan& p = plan.g[group];
+  if (index < 0 || index >= p.count) return fail(MA_ERR_INVALID_ARG, "index %d out of range", index);
+  const int ub = hp->ns_steps & 1;
+  *u = reinterpret_cast<unsigned char*>(workspace) + p.off_direct(ub) +
+       (size_t)((int64_t)index * p.x_stride * dt_bytes(p.dt_x));
+  *ld = p.ld_direct();
+  if (transposed) *transposed = 0;
+  *elem_bytes = (int32_t)dt_bytes(p.dt_x);
+  return MA_OK;
+}
+
+int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
+  if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
+  std::vector<Range> rs;
+  for (int i = 0; i < n; ++i) {
+    const ma_adamw_segment& S = segs[i];
+    if (S.n < 0) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0", i);
+    if (S.param_dtype != MA_F32 || S.grad_dtype != MA_F32)
+      return fail(MA_ERR_UNSUPPORTED, "segment %d: AdamW buffers must be MA_F32", i);
+    if (S.n == 0) continue;
+    if (!S.param || !S.grad || !S.exp_avg || !S.exp_avg_sq)
+      return fail(MA_ERR_INVALID_ARG, "segment %d: null device pointer", i);
+    if (((uintptr_t)S.param | (uintptr_t)S.grad | (uintptr_t)S.exp_avg | (uintptr_t)S.exp_avg_sq) & 3)
+      return fail(MA_ERR_INVALID_ARG, "segment %d: pointer not 4-byte aligned", i);
+    if (S.step < 1) return fail(MA_ERR_INVALID_ARG, "segment %d: step must be >= 1", i);
+    if (!std::isfinite(S.lr) || !std::isfinite(S.beta1) || !std::isfinite(S.beta2) || !std::isfinite(S.eps) ||
+        !std::isfinite(S.weight_decay) || S.beta1 < 0.f || S.beta1 >= 1.f || S.beta2 < 0.f || S.beta2 >= 1.f)
+      return fail(MA_ERR_INVALID_ARG, "segment %d: hyperparameters out of range", i);
+    const uintptr_t nb = (uintptr_t)S.n * 4;
+    rs.push_back({(uintptr_t)S.param, (uintptr_t)S.param + nb, 0});
+    rs.push_back({(uintptr_t)S.grad, (uintptr_t)S.grad + nb, 1});
+    rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, 2});
+    rs.push_back({(uintptr_t)S.exp_avg_sq, (uintptr_t)S.exp_avg_sq + nb, 2});
+  }
+  int rc = check_overlaps(rs);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  AdamArgs A{};
+  int64_t blocks = 0;
+  auto flush = [&]() -> int {
+    if (A.nseg == 0) return MA_OK;
+    A.total_blocks = (int32_t)blocks;
+    hipError_t err;
+    {
+      ProfScope ps(MA_K_ADAMW, s);
+      err = launch_adamw(A, s);
+    }
+    A = AdamArgs{};
+    blocks = 0;
+    return err == hipSuccess ? MA_OK : hip_fail(err, "AdamW launch");
+  };
+  for (int i = 0; i < n; ++i) {
+    const ma_adamw_segment& S = segs[i];
+    if (S.n == 0) continue;
+    const int64_t nb = (S.n + kAdamBlockElems - 1) / kAdamBlockElems;
+    if (A.nseg == kMaxAdamSegs || blocks + nb > (int64_t)0x7fffffff) {
+      if ((rc = flush())) return rc;
+    }
+    AdamSeg& D = A.s[A.nseg++];
+    D.p = reinterpret_cast<float*>(S.param);
+    D.g = reinterpret_cast<const float*>(S.grad);
+    D.m = reinterpret_cast<float*>(S.exp_avg);
+    D.v = reinterpret_cast<float*>(S.exp_avg_sq);
+    D.n = S.n;
+    D.block_begin = blocks;
+    const double lr = S.lr, b1 = S.beta1, b2 = S.beta2, wd = S.weight_decay;
+    const double t = (double)S.step;
+    D.cd = (float)(1.0 - lr * wd);
+    D.b1 = (float)b1;
+    D.b2 = (float)b2;
+    D.c1 = (float)(1.0 - b1);
+    D.c2 = (float)(1.0 - b2);
+    D.ss = (float)(lr / (1.0 - std::pow(b1, t)));
+    D.s2 = (float)std::sqrt(1.0 - std::pow(b2, t));
+    D.eps = S.eps;
+    D.decay = S.weight_decay != 0.0f ? 1 : 0;
+    D.vec = aligned16(S.param) && aligned16(S.grad) && aligned16(S.exp_avg) && aligned16(S.exp_avg_sq);
+    blocks += nb;
+  }
+  return flush();
+}
+
+// ---------------------------------------------------------------------------
+// stage entry points
+// ---------------------------------------------------------------------------
+int ma_test_bf16_round(const float* in, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!in || !out))) return fail(MA_ERR_INVALID_ARG, "null buffer or n < 0");
+  hipError_t err = launch_bf16_round(in, out, n, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MA_OK : hip_fail(err, "bf16 round launch");
+}
+
+int ma_test_muon_momentum(const ma_muon_group* group, float beta, int32_t nesterov, float* mt_out,
+                          void* stream) {
+  if (!group || !mt_out) return fail(MA_ERR_INVALID_ARG, "null argument");
+  int rc = validate_group(*group, 0, true);
+  if (rc) return rc;
+  if (!std::isfinite(beta)) return fail(MA_ERR_INVALID_ARG, "beta is not finite");
+  const ma_muon_group& g = *group;
+  for (int first = 0; first < g.count; first += kMaxMatsPerLaunch) {
+    const int cnt = std::min(kMaxMatsPerLaunch, g.count - first);
+    ElemArgs a{};
+    a.R = (int32_t)g.rows;
+    a.C = (int32_t)g.cols;
+    a.count = cnt;
+    a.r_ext = a.R;
+    a.c_ext = a.C;
+    a.tiles_r = (int32_t)((g.rows + 63) / 64);
+    a.tiles_c = (int32_t)((g.cols + 63) / 64);
+    a.x_stride = g.rows * g.cols;
+    a.xd = mt_out + (size_t)first * a.x_stride;
+    a.ld_d = g.cols;
+    a.beta = beta;
+    a.nesterov = nesterov ? 1 : 0;
+    bool vec = (g.cols % 8) == 0 && aligned16(a.xd);
+    for (int i = 0; i < cnt; ++i) {
+      a.mat[i].g = g.grads[first + i];
+      a.mat[i].m = g.momentum[first + i];
+      vec = vec && aligned16(a.mat[i].g) && aligned16(a.mat[i].m);
+    }
+    a.vec = vec;
+    hipError_t err = launch_pre(g.grad_dtype, g.mom_dtype, DT_F32, a, reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "momentum stage launch");
+  }
+  return MA_OK;
+}
+
+int ma_test_muon_update(const ma_muon_group* group, const void* u, int32_t u_dtype, float c_lr, float c_wd,
+                        int32_t cautious, int32_t decay, void* stream) {
+  if (!group || !u) return fail(MA_ERR_INVALID_ARG, "null argument");
+  int rc = validate_group(*group, 0, true);
+  if (rc) return rc;
+  if (!dt_valid(u_dtype)) return fail(MA_ERR_UNSUPPORTED, "u_dtype %d", u_dtype);
+  const ma_muon_group& g = *group;
+  const int64_t ue = dt_bytes(u_dtype);
+  for (int first = 0; first < g.count; first += kMaxMatsPerLaunch) {
+    const int cnt = std::min(kMaxMatsPerLaunch, g.count - first);
+    ElemArgs a{};
+    a.R = (int32_t)g.rows;
+    a.C = (int32_t)g.cols;
+    a.count = cnt;
+    a.tiles_r = (int32_t)((g.rows + 63) / 64);
+    a.tiles_c = (int32_t)((g.cols + 63) / 64);
+    a.x_stride = g.rows * g.cols;
+    a.xd = (void*)((const unsigned char*)u + (size_t)(first * a.x_stride * ue));
+    a.ld_d = g.cols;
+    a.c_lr = c_lr;
+    a.c_wd = c_wd;
+    a.cautious = cautious ? 1 : 0;
+    a.decay = decay ? 1 : 0;
+    bool vec = (g.cols % 8) == 0 && aligned16(a.xd);
+    for (int i = 0; i < cnt; ++i) {
+      a.mat[i].w = g.params[first + i];
+      vec = vec && aligned16(a.mat[i].w);
+    }
+    a.vec = vec;
+    hipError_t err = launch_post(g.param_dtype, u_dtype, a, reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "update stage launch");
+  }
+  return MA_OK;
+}
+
+size_t ma_test_ns_workspace_size(int64_t m, int64_t n, int32_t count, int32_t precision) {
+  if (m <= 0 || n < m || count < 0 || !dt_valid(precision)) {
+    fail(MA_ERR_INVALID_ARG, "need 0 < m <= n, count >= 0, valid precision");
+    return 0;
+  }
+  GroupPlan p{};
+  size_t off = 0;
+  plan_group(p, m, n, count, precision, off);
+  return off;
+}
+
+int ma_test_ns(int64_t m, int64_t n, int32_t count, int32_t precision, const void* x0, void* u,
+               const float* abc, int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream) {
+  if (m <= 0 || n < m || count < 0 || !dt_valid(precision))
+    return fail(MA_ERR_INVALID_ARG, "need 0 < m <= n, count >= 0, valid precision");
+  if (m * n > (int64_t)1 << 31) return fail(MA_ERR_INVALID_ARG, "matrix too large");
+  if (count > 0 && (!x0 || !u)) return fail(MA_ERR_INVALID_ARG, "null buffer");
+  if (ns_steps < 0 || ns_steps > MA_MAX_NS_STEPS || (ns_steps > 0 && !abc))
+    return fail(MA_ERR_INVALID_ARG, "bad ns_steps or abc");
+  Plan plan;
+  plan.g.resize(1);
+  GroupPlan& p = plan.g[0];
+  size_t off = 0;
+  plan_group(p, m, n, count, precision, off);
+  p.dt_p = p.dt_g = p.dt_m = precision;
+  p.src = nullptr;
+  if (!workspace || workspace_bytes < off || (uintptr_t)workspace % MA_WORKSPACE_ALIGN)
+    return fail(MA_ERR_WORKSPACE, "workspace null, misaligned or smaller than %zu bytes", off);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  const int64_t e = dt_bytes(precision);
+  hipError_t err;
+  // pack x0 into the padded X / X^T buffers
+  for (int first = 0; first < count; first += kMaxMatsPerLaunch) {
+    const int cnt = std::min(kMaxMatsPerLaunch, count - first);
+    ElemArgs a{};
+    a.R = (int32_t)m;
+    a.C = (int32_t)n;
+    a.count = cnt;
+    a.r_ext = (int32_t)p.r_ext;
+    a.c_ext = (int32_t)p.c_ext;
+    a.tiles_r = (int32_t)(p.r_ext / 64);
+    a.tiles_c = (int32_t)(p.c_ext / 64);
+    a.x_stride = p.x_stride;
+    a.xd = ws + p.off_x[0] + (size_t)(first * p.x_stride * e);
+    a.xt = ws + p.off_xt[0] + (size_t)(first * p.x_stride * e);
+    a.ld_d = p.n_pad;
+    a.ld_t = p.m_pad;
+    a.pure_copy = 1;
+    for (int i = 0; i < cnt; ++i) a.mat[i].g = (const unsigned char*)x0 + (size_t)((first + i) * m * n * e);
+    if ((err = launch_pre(precision, precision, precision, a, s)) != hipSuccess) return hip_fail(err, "pack");
+  }
+  int rc = enqueue_ns(plan, ws, abc, ns_steps, precision, s);
+  if (rc) return rc;
+  const int ub = ns_steps & 1;
+  for (int i = 0; i < count; ++i) {
+    err = hipMemcpy2DAsync((unsigned char*)u + (size_t)(i * m * n * e), (size_t)(n * e),
+                           ws + p.off_x[ub] + (size_t)(i * p.x_stride * e), (size_t)(p.n_pad * e),
+                           (size_t)(n * e), (size_t)m, hipMemcpyDeviceToDevice, s);
+    if (err != hipSuccess) return hip_fail(err, "copy-out");
+  }
+  return MA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Shared device helpers and launch descriptors of the Muon + AdamW library.
+// Target: AMD Instinct MI355X (gfx950, CDNA4), 64-lane wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace ma {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kPad = 256;          // workspace matrices are padded to multiples of this
+constexpr int kMaxMatsPerLaunch = 64;
+
+// storage codes (match ma_dtype)
+constexpr int DT_F32 = 0;
+constexpr int DT_BF16 = 1;
+
+__host__ __device__ constexpr int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// ----------------------------------------------------------------------------
+// bf16 <-> fp32
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low|high<<16
+// (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+// load / store n consecutive elements of storage type DT as fp32 (n = 8: one
+// 16-byte vector for bf16, two for fp32). Pointers must be 16-byte aligned.
+template <int DT>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+  if constexpr (DT == DT_BF16) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(void* p, const float (&v)[8]) {
+  if constexpr (DT == DT_BF16) {
+    uint4 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = u;
+  } else {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load1(const void* p, int64_t i) {
+  if constexpr (DT == DT_BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void store1(void* p, int64_t i, float x) {
+  if constexpr (DT == DT_BF16) reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
+  else reinterpret_cast<float*>(p)[i] = x;
+}
+
+template <int DT> constexpr int elem_bytes() { return DT == DT_BF16 ? 2 : 4; }
+
+// ----------------------------------------------------------------------------
+// wavefront reduction (fixed order: butterfly over the 64 lanes)
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+}  // namespace ma

@@ -1,0 +1,351 @@
+// Muon elementwise and reduction kernels (gfx950), HBM-bound.
+//
+//   k_rowsumsq_momentum  per row of the Nesterov look-ahead Mt = G + beta*m1,
+//                        m1 = beta*M + G: sum of squares (one wave per row,
+//                        16-byte loads, butterfly shuffle reduction; no atomics)
+//   k_finalize           per matrix: Frobenius scale, MuonEq row factors
+//   k_pre                momentum update M <- m1 (stored), X0 = Mt * f_row,
+//                        written in the parameter's layout and transposed
+//                        (through an LDS tile) into the Newton-Schulz buffers
+//   k_post               cautious decoupled decay and the update, W <- W'
+//
+// Sources: momentum and look-ahead -- "Chapter 4: The MuonAdamW Optimizer",
+// section "The Muon Update Rule" and "3.9 Optimizers ...", section "From
+// Gradient Descent to Momentum"; Frobenius normalisation -- "Chapter 4",
+// section "Polar Express: Newton-Schulz Orthogonalization"; cautious mask,
+// MuonEq and the lr multiplier -- nanochat discussion "Stuck at the optimizer
+// after figuring out backward()", reply by mira687; decay before the update
+// -- "Chapter 4", section "The Full Muon Step".
+//
+// The elementwise arithmetic is binary32 with one rounding per operation and
+// no contraction (this file is built with -ffp-contract=off); stores to bf16
+// round to nearest even.
+#include "muon_elem.hpp"
+
+namespace ma {
+
+template <int DT>
+__device__ __forceinline__ const void* eptr(const void* base, int64_t i) {
+  return reinterpret_cast<const unsigned char*>(base) + i * elem_bytes<DT>();
+}
+template <int DT>
+__device__ __forceinline__ void* eptr(void* base, int64_t i) {
+  return reinterpret_cast<unsigned char*>(base) + i * elem_bytes<DT>();
+}
+
+// m1 = beta*m + g;  mt = nesterov ? g + beta*m1 : m1
+__device__ __forceinline__ void momentum1(float g, float m, float beta, int nesterov, float& m1,
+                                          float& mt) {
+  m1 = __fadd_rn(__fmul_rn(beta, m), g);
+  mt = nesterov ? __fadd_rn(g, __fmul_rn(beta, m1)) : m1;
+}
+
+constexpr int kRowsPerBlock = 16;
+
+template <int DTG, int DTM>
+__global__ void __launch_bounds__(256) k_rowsumsq_momentum(const ElemArgs a) {
+  const int bpm = (a.R + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int k = blockIdx.x / bpm;
+  const int rb = blockIdx.x - k * bpm;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const void* gp = a.mat[k].g;
+  const void* mp = a.mat[k].m;
+  for (int rr = wave; rr < kRowsPerBlock; rr += 4) {
+    const int r = rb * kRowsPerBlock + rr;
+    if (r >= a.R) break;
+    const int64_t base = (int64_t)r * a.C;
+    float acc = 0.0f;
+    if (a.vec) {
+      for (int c = lane * 8; c < a.C; c += 512) {
+        float g[8], m[8];
+        load8<DTG>(eptr<DTG>(gp, base + c), g);
+        load8<DTM>(eptr<DTM>(mp, base + c), m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float m1, mt;
+          momentum1(g[e], m[e], a.beta, a.nesterov, m1, mt);
+          acc = __builtin_fmaf(mt, mt, acc);
+        }
+      }
+    } else {
+      for (int c = lane; c < a.C; c += 64) {
+        float m1, mt;
+        momentum1(load1<DTG>(gp, base + c), load1<DTM>(mp, base + c), a.beta, a.nesterov, m1, mt);
+        acc = __builtin_fmaf(mt, mt, acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = acc;
+  }
+}
+
+// Row sums of squares of a workspace buffer in the parameter's layout (the
+// update U, for MuonEq POST).
+template <int DTX>
+__global__ void __launch_bounds__(256) k_rowsumsq_buffer(const ElemArgs a) {
+  const int bpm = (a.R + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int k = blockIdx.x / bpm;
+  const int rb = blockIdx.x - k * bpm;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const void* xp = eptr<DTX>(static_cast<const void*>(a.xd), (int64_t)k * a.x_stride);
+  for (int rr = wave; rr < kRowsPerBlock; rr += 4) {
+    const int r = rb * kRowsPerBlock + rr;
+    if (r >= a.R) break;
+    const int64_t base = (int64_t)r * a.ld_d;
+    float acc = 0.0f;
+    // the buffer pitch is a multiple of 256; columns C.. are zero
+    for (int c = lane * 8; c < a.C; c += 512) {
+      float x[8];
+      load8<DTX>(eptr<DTX>(xp, base + c), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = acc;
+  }
+}
+
+// One block per matrix; fixed-order reduction (strided partial sums, then an
+// LDS tree), so results do not depend on scheduling.
+__global__ void __launch_bounds__(256) k_finalize(const ElemArgs a) {
+  __shared__ float red[256];
+  const int k = blockIdx.x;
+  const float* rs = a.rowsq + (int64_t)k * a.row_stride;
+  float* rf = a.rowf + (int64_t)k * a.row_stride;
+  const int t = threadIdx.x;
+  const int mode = a.finalize_mode;
+  float part = 0.0f;
+  for (int i = t; i < a.R; i += 256) {
+    const float q = rs[i];
+    if (mode == 1) {
+      const float n = sqrtf(q);
+      const float y = n / (n + a.eq_eps);   // norm of the equilibrated row
+      part += y * y;
+    } else {
+      part += q;
+    }
+  }
+  red[t] = part;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  const float total = red[0];
+  if (mode == 0) {
+    const float s = 1.0f / (sqrtf(total) + a.norm_eps);
+    for (int i = t; i < a.R; i += 256) rf[i] = s;
+  } else if (mode == 1) {
+    const float s = 1.0f / (sqrtf(total) + a.norm_eps);
+    for (int i = t; i < a.R; i += 256) rf[i] = s / (sqrtf(rs[i]) + a.eq_eps);
+  } else {
+    const float rho = sqrtf(total) / sqrtf((float)a.R);
+    for (int i = t; i < a.R; i += 256) rf[i] = rho / (sqrtf(rs[i]) + a.eq_eps);
+  }
+}
+
+// 64 x 64 tiles of the parameter layout; thread t covers rows t/8 and t/8+32,
+// columns 8*(t%8) .. +7 of its tile.
+template <int DTG, int DTM, int DTX>
+__global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
+  __shared__ float tile[64][65];
+  const int tiles = a.tiles_r * a.tiles_c;
+  const int k = blockIdx.x / tiles;
+  const int t = blockIdx.x - k * tiles;
+  const int tr = t / a.tiles_c, tc = t - tr * a.tiles_c;
+  const int r0 = tr * 64, c0 = tc * 64;
+  const void* gp = a.mat[k].g;
+  void* mp = a.mat[k].m;
+  const int tid = threadIdx.x;
+  const int cl = (tid & 7) * 8;
+  const bool vec = a.vec != 0;
+  void* xd = eptr<DTX>(a.xd, (int64_t)k * a.x_stride);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rl = (tid >> 3) + 32 * h;
+    const int r = r0 + rl, c = c0 + cl;
+    float x[8];
+    if (r < a.R && c < a.C) {
+      const float f = a.rowf ? a.rowf[(int64_t)k * a.row_stride + r] : 1.0f;
+      const int64_t off = (int64_t)r * a.C + c;
+      if (a.pure_copy) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = c + e < a.C ? load1<DTG>(gp, off + e) : 0.0f;
+      } else if (vec) {
+        float g[8], m[8], m1[8];
+        load8<DTG>(eptr<DTG>(gp, off), g);
+        load8<DTM>(eptr<DTM>(static_cast<const void*>(mp), off), m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float mt;
+          momentum1(g[e], m[e], a.beta, a.nesterov, m1[e], mt);
+          x[e] = __fmul_rn(mt, f);
+        }
+        store8<DTM>(eptr<DTM>(mp, off), m1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (c + e < a.C) {
+            float m1, mt;
+            momentum1(load1<DTG>(gp, off + e), load1<DTM>(mp, off + e), a.beta, a.nesterov, m1, mt);
+            store1<DTM>(mp, off + e, m1);
+            x[e] = __fmul_rn(mt, f);
+          } else {
+            x[e] = 0.0f;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    }
+    if (r < a.r_ext) {
+      const int64_t off = (int64_t)r * a.ld_d + c;
+      if (c + 8 <= a.c_ext && (a.ld_d & 7) == 0) {
+        store8<DTX>(eptr<DTX>(xd, off), x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c + e < a.c_ext) store1<DTX>(xd, off + e, x[e]);
+      }
+    }
+    if (a.xt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[rl][cl + e] = x[e];
+    }
+  }
+  if (a.xt) {
+    // transposed copy: row (c0 + cc) of xt holds column cc of the tile
+    __syncthreads();
+    void* xt = eptr<DTX>(a.xt, (int64_t)k * a.x_stride);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cc = (tid >> 3) + 32 * h;
+      const int rr = (tid & 7) * 8;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = tile[rr + e][cc];
+      store8<DTX>(eptr<DTX>(xt, (int64_t)(c0 + cc) * a.ld_t + r0 + rr), y);
+    }
+  }
+}
+
+// W <- RNE( (mask ? W - c_wd*W : W) - c_lr*U ), mask = cautious ? (U*W >= 0) : 1.
+template <int DTP, int DTX>
+__global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
+  const int tiles = a.tiles_r * a.tiles_c;
+  const int k = blockIdx.x / tiles;
+  const int t = blockIdx.x - k * tiles;
+  const int tr = t / a.tiles_c, tc = t - tr * a.tiles_c;
+  const int r0 = tr * 64, c0 = tc * 64;
+  void* wp = a.mat[k].w;
+  const void* xd = eptr<DTX>(static_cast<const void*>(a.xd), (int64_t)k * a.x_stride);
+  const int tid = threadIdx.x;
+  const int cl = (tid & 7) * 8;
+  const bool vec = a.vec && (a.ld_d & 7) == 0;
+  const float clr = a.c_lr, cwd = a.c_wd;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + (tid >> 3) + 32 * h, c = c0 + cl;
+    if (r >= a.R || c >= a.C) continue;
+    const float f = a.rowf ? a.rowf[(int64_t)k * a.row_stride + r] : 1.0f;
+    const int64_t off = (int64_t)r * a.C + c;
+    const int64_t uoff = (int64_t)r * a.ld_d + c;
+    float w[8], u[8];
+    const int n = vec ? 8 : (a.C - c < 8 ? a.C - c : 8);
+    if (vec) {
+      load8<DTP>(eptr<DTP>(static_cast<const void*>(wp), off), w);
+      load8<DTX>(eptr<DTX>(xd, uoff), u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w[e] = e < n ? load1<DTP>(wp, off + e) : 0.0f;
+        u[e] = e < n ? load1<DTX>(xd, uoff + e) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ue = a.rowf ? __fmul_rn(u[e], f) : u[e];
+      const bool mask = a.cautious ? (__fmul_rn(ue, w[e]) >= 0.0f) : true;
+      const float w1 = (a.decay && mask) ? __fsub_rn(w[e], __fmul_rn(cwd, w[e])) : w[e];
+      w[e] = __fsub_rn(w1, __fmul_rn(clr, ue));
+    }
+    if (vec) {
+      store8<DTP>(eptr<DTP>(wp, off), w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < n) store1<DTP>(wp, off + e, w[e]);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_bf16_round(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = f32_to_bf16(in[i]);
+}
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+#define MA_DISPATCH2(d1, d2, KER, ...)                                                  \
+  do {                                                                                  \
+    if ((d1) == DT_BF16 && (d2) == DT_BF16) hipLaunchKernelGGL((KER<DT_BF16, DT_BF16>), __VA_ARGS__); \
+    else if ((d1) == DT_BF16) hipLaunchKernelGGL((KER<DT_BF16, DT_F32>), __VA_ARGS__);  \
+    else if ((d2) == DT_BF16) hipLaunchKernelGGL((KER<DT_F32, DT_BF16>), __VA_ARGS__);  \
+    else hipLaunchKernelGGL((KER<DT_F32, DT_F32>), __VA_ARGS__);                         \
+  } while (0)
+
+hipError_t launch_rowsumsq_momentum(int dt_g, int dt_m, const ElemArgs& a, hipStream_t s) {
+  const int blocks = a.count * ((a.R + kRowsPerBlock - 1) / kRowsPerBlock);
+  if (blocks <= 0) return hipSuccess;
+  MA_DISPATCH2(dt_g, dt_m, k_rowsumsq_momentum, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowsumsq_buffer(int dt_x, const ElemArgs& a, hipStream_t s) {
+  const int blocks = a.count * ((a.R + kRowsPerBlock - 1) / kRowsPerBlock);
+  if (blocks <= 0) return hipSuccess;
+  if (dt_x == DT_BF16) hipLaunchKernelGGL((k_rowsumsq_buffer<DT_BF16>), dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_rowsumsq_buffer<DT_F32>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const ElemArgs& a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_finalize, dim3(a.count), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DTX>
+static void launch_pre_x(int dt_g, int dt_m, const ElemArgs& a, int blocks, hipStream_t s) {
+  if (dt_g == DT_BF16 && dt_m == DT_BF16) hipLaunchKernelGGL((k_pre<DT_BF16, DT_BF16, DTX>), dim3(blocks), dim3(256), 0, s, a);
+  else if (dt_g == DT_BF16) hipLaunchKernelGGL((k_pre<DT_BF16, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a);
+  else if (dt_m == DT_BF16) hipLaunchKernelGGL((k_pre<DT_F32, DT_BF16, DTX>), dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_pre<DT_F32, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a);
+}
+
+hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s) {
+  const int blocks = a.count * a.tiles_r * a.tiles_c;
+  if (blocks <= 0) return hipSuccess;
+  if (dt_x == DT_BF16) launch_pre_x<DT_BF16>(dt_g, dt_m, a, blocks, s);
+  else launch_pre_x<DT_F32>(dt_g, dt_m, a, blocks, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_post(int dt_p, int dt_x, const ElemArgs& a, hipStream_t s) {
+  const int blocks = a.count * a.tiles_r * a.tiles_c;
+  if (blocks <= 0) return hipSuccess;
+  MA_DISPATCH2(dt_p, dt_x, k_post, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_bf16_round, dim3((unsigned)blocks), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace ma

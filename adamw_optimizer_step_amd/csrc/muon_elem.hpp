@@ -1,0 +1,45 @@
+// Launch descriptors of the Muon elementwise and reduction kernels.
+#pragma once
+#include "common.hpp"
+
+namespace ma {
+
+struct MatPtr {
+  const void* g;   // gradient (param layout)
+  void* m;         // momentum buffer (param layout)
+  void* w;         // weight (param layout)
+};
+
+// One launch covers up to kMaxMatsPerLaunch matrices of one shape group.
+struct ElemArgs {
+  int32_t R, C;              // parameter shape (rows x cols)
+  int32_t count;             // matrices in this launch
+  int32_t r_ext, c_ext;      // param-layout extent the tile grid covers (>= R, C)
+  int32_t tiles_r, tiles_c;  // 64 x 64 tiles per matrix
+  // workspace views of matrix k start k*x_stride elements after the bases
+  void* xd;                  // copy in the parameter's layout, row pitch ld_d
+  void* xt;                  // transposed copy (may be null), row pitch ld_t
+  int64_t ld_d, ld_t, x_stride;
+  float* rowsq;              // per-row sums of squares, matrix k at k*row_stride
+  float* rowf;               // per-row factors (null: 1)
+  int64_t row_stride;
+  float beta;
+  int32_t nesterov;
+  float c_lr, c_wd;
+  int32_t cautious, decay;
+  float norm_eps, eq_eps;
+  int32_t finalize_mode;     // 0: Frobenius only, 1: MuonEq pre, 2: MuonEq post
+  int32_t vec;               // C % 8 == 0 and every matrix pointer 16-byte aligned
+  int32_t pure_copy;         // k_pre: X0 = G (no momentum; M untouched)
+  MatPtr mat[kMaxMatsPerLaunch];
+};
+
+// dtype codes: DT_F32 / DT_BF16
+hipError_t launch_rowsumsq_momentum(int dt_g, int dt_m, const ElemArgs& a, hipStream_t s);
+hipError_t launch_rowsumsq_buffer(int dt_x, const ElemArgs& a, hipStream_t s);
+hipError_t launch_finalize(const ElemArgs& a, hipStream_t s);
+hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s);
+hipError_t launch_post(int dt_p, int dt_x, const ElemArgs& a, hipStream_t s);
+hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+
+}  // namespace ma

@@ -1,0 +1,48 @@
+// Launch descriptors of the Newton-Schulz GEMM kernels.
+#pragma once
+#include "common.hpp"
+
+namespace ma {
+
+// Epilogues of C = P Q^T (fp32 accumulation), one per sub-step of a quintic
+// Newton-Schulz step X <- a X + (b A + c A A) X with A = X X^T:
+enum NsEpilogue : int {
+  EPI_GRAM = 0,  // A = X X^T                (symmetric: upper tiles, mirrored)
+  EPI_POLY = 1,  // B = b*A + c*(A A^T)      (A symmetric, so A A^T = A A; mirrored)
+  EPI_AXPY = 2,  // X' = a*X + B X           (Q = X^T; writes X' and/or X'^T)
+};
+
+constexpr int kMaxNsGroups = 8;
+
+// One shape group of a batched launch: `count` independent products.
+// Element strides between consecutive matrices are s*, row pitches ld*.
+struct NsGroup {
+  const void* P;    // rows i, K contiguous
+  const void* Q;    // rows j, K contiguous
+  const void* E;    // epilogue input read as E[j][i] (A for POLY, X^T for AXPY)
+  void* outN;       // C[i][j] (row-major output), may be null
+  void* outT;       // C[j][i] (transposed output), may be null
+  int64_t sP, sQ, sE, sN, sT;
+  int32_t ldP, ldQ, ldE, ldN, ldT;
+  int32_t K;        // reduction length (multiple of the K tile)
+  int32_t tm, tn;   // output tile grid
+  int32_t tiles;    // tiles per matrix
+  int32_t count;
+  int32_t block_begin;
+  int32_t symmetric;  // 1: only tiles bi <= bj, mirrored through outN/outT
+};
+
+struct NsArgs {
+  int32_t n_groups;
+  int32_t total_jobs;
+  int32_t padded_blocks;   // multiple of 8 (XCD round-robin remap)
+  float a, b, c;
+  NsGroup g[kMaxNsGroups];
+};
+
+// tile configuration chosen per launch
+struct NsTile { int bm, bn, bk; };
+
+hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& args, hipStream_t s);
+
+}  // namespace ma

@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark: full Muon + AdamW optimizer steps per second on one MI355X.
+
+One step = ``ma_muon_step`` over every weight matrix of the parameter set
+(momentum, Frobenius / MuonEq normalisation, quintic Newton-Schulz, cautious
+decay and update) plus ``ma_adamw_step`` over the embedding buffers, on
+synthetic seeded inputs already resident in HBM. Default workload: the
+12-layer d=1024 parameter set (48 x 1024^2, 12 x 4096x1024, 12 x 1024x4096
+Muon matrices in bf16; wte and lm_head 50304x1024 AdamW in fp32).
+
+Prints one JSON line (rank 0). The ``roofline`` object reports the dominant
+kernel (by time) against its roofline, from HIP events recorded around each
+launch on the launch stream during the timed steps; ``cpu_baseline`` times
+the oracle on a bounded sample of the same workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3_12L_d1024")
+    ap.add_argument("--ns-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--no-profile", action="store_true", help="time without per-kernel events")
+    return ap.parse_args()
+
+
+def elem_bytes(dt):
+    return 2 if dt == "bf16" else 4
+
+
+def work_model(wl, ns_steps):
+    """Algorithmic work per launch of each kernel kind (per step for the rest)."""
+    ex = elem_bytes(wl.ns_precision)
+    ep, eg, em = elem_bytes(wl.param_dtype), elem_bytes(wl.grad_dtype), elem_bytes(wl.mom_dtype)
+    gram = poly = axpy = 0.0
+    pre = rown = post = 0.0
+    for g in wl.muon_groups:
+        m, n = min(g.rows, g.cols), max(g.rows, g.cols)
+        gram += g.count * m * m * n          # A = X X^T, symmetric: m^2 n
+        poly += g.count * m * m * m          # A A, symmetric: m^3
+        axpy += g.count * 2.0 * m * m * n    # B X: 2 m^2 n
+        e = g.rows * g.cols * g.count
+        rown += e * (eg + em)                # read G, M
+        pre += e * (eg + 2 * em + 2 * ex)    # read G, M; write M, X0, X0^T
+        post += e * (2 * ep + ex)            # read W, U; write W
+    adam = 28.0 * wl.adamw_numel
+    return {
+        "gram": ("TFLOP/s", gram), "poly": ("TFLOP/s", poly), "axpy": ("TFLOP/s", axpy),
+        "rownorm": ("GB/s", rown), "pre": ("GB/s", pre), "post": ("GB/s", post), "adamw": ("GB/s", adam),
+        "ns_total_flops_per_step": ns_steps * (gram + poly + axpy),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs the optimizer step on one GPU; "
+                                   f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import adamw_optimizer_step_amd as M
+    from adamw_optimizer_step_amd import _lib as L
+    from workloads import materialize, workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workload(args.config)
+    T = args.ns_steps if args.ns_steps is not None else wl.ns_steps
+    t0 = time.time()
+    data = materialize(wl, device=dev, seed=0)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {wl.name} built in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    groups = [M.MuonGroup(d["W"], d["G"], d["M"]) for d in data["muon"]]
+    hp = M.MuonHParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
+                       ns_steps=T, coeffs=M.KELLER_JORDAN, cautious=wl.cautious, equilibrate=wl.equilibrate,
+                       ns_precision=wl.ns_precision, lr_scale=wl.lr_scale)
+    ws = torch.empty(max(1, M.muon_workspace_size(groups, hp)), dtype=torch.uint8, device=dev)
+    segs = []
+    for a in data["adamw"]:
+        s = a["spec"]
+        segs.append(dict(param=a["p"], grad=a["g"], exp_avg=a["m"], exp_avg_sq=a["v"], step=a["step"],
+                         lr=s.lr, beta1=s.beta1, beta2=s.beta2, eps=s.eps, weight_decay=s.weight_decay))
+
+    def step(i):
+        M.muon_step(groups, hp, workspace=ws)
+        if segs:
+            for s in segs:
+                s["step"] = wl.adamw_step + i
+            M.adamw_step(segs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    lib = L.lib()
+    profile = not args.no_profile
+    if profile:
+        L.check(lib.ma_profile_begin(args.steps * 64 + 64))
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if profile:
+        L.check(lib.ma_profile_end())
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel durations from the events recorded around each launch
+    import ctypes as C
+    model = work_model(wl, T)
+    kernels = {}
+    if profile:
+        for kind, name in enumerate(L.KERNEL_KINDS):
+            tot, n = C.c_double(), C.c_int64()
+            L.check(lib.ma_profile_read(kind, C.byref(tot), C.byref(n)))
+            if n.value == 0:
+                continue
+            avg_ms = tot.value / n.value
+            rec = {"ms_per_launch": round(avg_ms, 5), "launches_per_step": n.value / args.steps,
+                   "ms_per_step": round(tot.value / args.steps, 4)}
+            if name in model:
+                unit, work = model[name]
+                # elementwise kinds launch once per group chunk: spread the step's work
+                per_launch = work * (args.steps / n.value) if unit == "GB/s" else work
+                if unit == "TFLOP/s":
+                    rec.update(achieved=round(per_launch / (avg_ms * 1e-3) / 1e12, 2), unit=unit)
+                else:
+                    rec.update(achieved=round(per_launch / (avg_ms * 1e-3) / 1e9, 1), unit=unit)
+            kernels[name] = rec
+
+    ns_ms = sum(kernels[k]["ms_per_step"] for k in ("gram", "poly", "axpy") if k in kernels)
+    peak_f = PEAK_BF16_TFLOPS if wl.ns_precision == "bf16" else PEAK_F32_TFLOPS
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        r = kernels[dom]
+        bound = "mfma" if r.get("unit") == "TFLOP/s" else "hbm"
+        peak = peak_f if bound == "mfma" else PEAK_HBM_GBS
+        roofline = {"kernel": dom, "bound": bound, "achieved": r.get("achieved"), "peak": peak,
+                    "unit": r.get("unit"), "frac": round(r.get("achieved", 0) / peak, 4),
+                    "traffic": traffic_for(dom, wl.name)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, T, args.cpu_budget_s)
+    out = {
+        "metric": "Muon+AdamW full steps/sec at 12L d=1024; NS-GEMM MFMA util %; HBM GB/s",
+        "value": round(1000.0 / ms, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.ns_precision == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "ns_steps": T,
+                   "coefficients": "Keller Jordan (3.4445, -4.7750, 2.0315) each step",
+                   "muon_matrices": sum(g.count for g in wl.muon_groups),
+                   "muon_elements": wl.muon_numel, "adamw_elements": wl.adamw_numel,
+                   "parallelism": "single GPU", "timing": "per-kernel HIP events inside the timed steps"
+                   if profile else "no per-kernel events"},
+        "roofline": roofline,
+        "ns_gemm": {"tflops_per_step": round(model["ns_total_flops_per_step"] / 1e12, 4),
+                    "ms_per_step": round(ns_ms, 4),
+                    "achieved_tflops": round(model["ns_total_flops_per_step"] / (ns_ms * 1e-3) / 1e12, 1) if ns_ms else None,
+                    "mfma_util": round(model["ns_total_flops_per_step"] / (ns_ms * 1e-3) / 1e12 / peak_f, 4) if ns_ms else None},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def traffic_for(kernel, workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        import hashlib
+        src = os.path.join(ROOT, rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, T, budget_s):
+    """The oracle, as it stands, on a bounded sample of the workload, scaled to
+    whole steps per second."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from workloads import materialize
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sample = materialize(wl.scaled(adamw_segments=()), device="cpu", seed=0, max_count=1)
+    spent = 0.0
+    per_group = []
+    for d, g in zip(sample["muon"], wl.muon_groups):
+        W, G, Mo = (d[k][0].float().numpy() for k in ("W", "G", "M"))
+        t0 = time.perf_counter()
+        O.muon_step(W, G, Mo, lr=wl.lr, momentum=wl.momentum, nesterov=wl.nesterov, coeffs=O.KELLER_JORDAN,
+                    ns_steps=T, weight_decay=wl.weight_decay, cautious=wl.cautious, equilibrate=wl.equilibrate,
+                    precision="bf16" if wl.ns_precision == "bf16" else "f64", param_dtype=wl.param_dtype,
+                    mom_dtype=wl.mom_dtype)
+        dt = time.perf_counter() - t0
+        spent += dt
+        per_group.append((g, dt))
+    adam_n = min(wl.adamw_numel, 1 << 24)
+    adam_s = 0.0
+    if adam_n:
+        rng = np.random.default_rng(0)
+        p = (rng.standard_normal(adam_n) * 0.02).astype(np.float32)
+        g = (rng.standard_normal(adam_n) * 1e-3).astype(np.float32)
+        m = (rng.standard_normal(adam_n) * 3e-4).astype(np.float32)
+        v = (g * g).astype(np.float32)
+        t0 = time.perf_counter()
+        O.adamw_step(p, g, m, v, 10, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0)
+        adam_s = time.perf_counter() - t0
+    est = sum(g.count * dt for g, dt in per_group) + adam_s * (wl.adamw_numel / max(adam_n, 1))
+    return {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"one matrix of each of the {len(per_group)} shape groups through the oracle's full "
+                       f"Muon step ({'bf16 rounding points' if wl.ns_precision == 'bf16' else 'float64'}, "
+                       f"numpy BLAS) and {adam_n} AdamW elements; scaled by matrix and element counts "
+                       f"to one whole step ({spent + adam_s:.1f} s of CPU time measured)")}
+
+
+if __name__ == "__main__":
+    main()

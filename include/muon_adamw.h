@@ -1,0 +1,237 @@
+/*
+ * muon_adamw.h -- C ABI of the MI355X (gfx950) Muon + AdamW optimizer step.
+ *
+ * Two operations, both in place on caller-owned device memory, both
+ * asynchronous on the caller's HIP stream:
+ *
+ *   ma_muon_step   one Muon step over groups of same-shape weight matrices
+ *                  ("Chapter 4: The MuonAdamW Optimizer", sections "The Muon
+ *                  Update Rule", "Polar Express: Newton-Schulz
+ *                  Orthogonalization" and "The Full Muon Step"; nanochat
+ *                  discussion "Stuck at the optimizer after figuring out
+ *                  backward()", reply by mira687: per-step Polar Express
+ *                  coefficients, cautious weight decay, MuonEq, the
+ *                  max(1, rows/cols)^0.5 lr multiplier, stacked same-shape
+ *                  matrices);
+ *   ma_adamw_step  one AdamW step over flat buffers ("3.9 Optimizers: SGD,
+ *                  Adam, Adafactor, Lion, Muon & Shampoo", section
+ *                  "Implementing AdamW from scratch"; "Chapter 4", section
+ *                  "The AdamW Step").
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers; "host" pointers are
+ *     read during the call only and may be freed when it returns.
+ *   - The library allocates no device memory and keeps no state between
+ *     calls. Scratch memory is the caller's workspace.
+ *   - Matrices are row-major, rows x cols, contiguous (leading dimension ==
+ *     cols); rows are output features, cols input features.
+ *   - Return value: MA_OK (0) or a negative MA_ERR_* code. Every argument is
+ *     validated before the first launch, so a rejected call changes nothing.
+ *     A kernel fault surfaces at the caller's next synchronisation.
+ *     ma_last_error() returns a message for the calling thread's last
+ *     failure.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the default stream).
+ *   - Calls that overlap on one stream are ordered; concurrent calls on
+ *     different streams must not share buffers or a workspace.
+ */
+#ifndef MUON_ADAMW_H
+#define MUON_ADAMW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MA_OK 0
+#define MA_ERR_INVALID_ARG -1   /* null pointer, bad size, bad enum, aliasing */
+#define MA_ERR_UNSUPPORTED -2   /* dtype combination not provided */
+#define MA_ERR_WORKSPACE -3     /* workspace null, too small or misaligned */
+#define MA_ERR_HIP -4           /* a HIP runtime call or launch failed */
+
+typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
+
+/* MuonEq row equilibration. PRE divides each row (output feature, in the
+ * parameter's own layout) of the Nesterov look-ahead by its Euclidean norm
+ * (+eq_eps) before the Frobenius normalisation; POST rescales each row of
+ * the orthogonalised update to the matrix's mean row norm, ||U||_F/sqrt(rows),
+ * over (||U_i|| + eq_eps). */
+typedef enum { MA_EQ_OFF = 0, MA_EQ_ROWS_PRE = 1, MA_EQ_ROWS_POST = 2 } ma_eq;
+
+/* Per-matrix lr multiplier: NONE = 1, SQRT_MAX1_R_OVER_C = sqrt(max(1, rows/cols))
+ * (nanochat discussion, reply by mira687: x2 for c_fc, x1 for c_proj). */
+typedef enum { MA_SCALE_NONE = 0, MA_SCALE_SQRT_MAX1_R_OVER_C = 1 } ma_scale;
+
+/* One group: `count` matrices of identical shape rows x cols.
+ * params/grads/momentum are HOST arrays of `count` DEVICE pointers; matrix i
+ * of the group is params[i] (rows*cols elements of param_dtype), grads[i]
+ * (grad_dtype, read only) and momentum[i] (mom_dtype, updated in place). */
+typedef struct {
+  int64_t rows, cols;
+  int32_t count;
+  int32_t param_dtype, grad_dtype, mom_dtype; /* ma_dtype */
+  void* const* params;
+  const void* const* grads;
+  void* const* momentum;
+} ma_muon_group;
+
+/* Muon hyperparameters ("Chapter 4", section "The Full Muon Step"; the
+ * nanochat discussion for the coefficient table, cautious mask and MuonEq).
+ *   lr            base learning rate (multiplied per matrix by lr_scale)
+ *   momentum      beta of the sum-form buffer  m <- beta*m + G
+ *   weight_decay  decoupled decay; the applied factor is lr_eff*weight_decay
+ *   nesterov      1: orthogonalise G + beta*m (look-ahead), 0: orthogonalise m
+ *   ns_steps      number T of quintic steps, 0..MA_MAX_NS_STEPS
+ *   abc           HOST array of 3*ns_steps floats: (a_k, b_k, c_k) of step k,
+ *                 X <- a_k X + (b_k A + c_k A A) X with A = X X^T
+ *   cautious      1: decay only where update and weight agree in sign,
+ *                 mask = (U * W >= 0)
+ *   equilibrate   ma_eq
+ *   ns_precision  MA_BF16: iterate in bf16 with fp32 accumulation;
+ *                 MA_F32: iterate in fp32
+ *   lr_scale      ma_scale
+ *   norm_eps      added to the Frobenius norm (the pages use 1e-7)
+ *   eq_eps        added to each row norm by MuonEq (1e-7) */
+typedef struct {
+  float lr, momentum, weight_decay;
+  int32_t nesterov, ns_steps;
+  const float* abc;
+  int32_t cautious, equilibrate, ns_precision, lr_scale;
+  float norm_eps, eq_eps;
+} ma_muon_hparams;
+
+#define MA_MAX_NS_STEPS 16
+#define MA_WORKSPACE_ALIGN 256
+
+/* Bytes of device workspace ma_muon_step needs for these groups and
+ * hyperparameters (0 on invalid arguments; see ma_last_error). The
+ * workspace holds the normalised momentum and the Newton-Schulz iterates
+ * and Gram matrices of every matrix, padded to multiples of 256. */
+size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
+                              const ma_muon_hparams* hp);
+
+/* One Muon step for every matrix of every group. Per matrix W (R x C),
+ * gradient G, momentum buffer M, in this order:
+ *   m1 = beta*M + G (fp32); M <- m1 rounded to mom_dtype (RNE)
+ *   Mt = G + beta*m1 if nesterov else m1                      (fp32)
+ *   optional MuonEq PRE; X0 = Mt / (||Mt||_F + norm_eps)
+ *   if R > C the iteration runs on X0^T (layout, no extra copy)
+ *   T quintic steps with the caller's coefficient table
+ *   optional MuonEq POST; U = final iterate in W's layout
+ *   lr_eff = lr * multiplier(R, C)  (fp64 on the host, then fp32)
+ *   mask = cautious ? (U*W >= 0) : 1
+ *   W <- RNE( (mask ? W - (lr_eff*wd)*W : W) - lr_eff*U )   (fp32, no FMA)
+ * The decay term is skipped entirely when weight_decay == 0.
+ * Supported storage: param/grad/mom each MA_BF16 or MA_F32.
+ * workspace: DEVICE, >= ma_muon_workspace_size bytes, MA_WORKSPACE_ALIGN
+ * aligned. Parameter, gradient and momentum buffers must not overlap each
+ * other or the workspace (MA_ERR_INVALID_ARG is returned for overlaps among
+ * the pointers passed). */
+int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Where matrix `index` of group `group` keeps the result of its Newton-Schulz
+ * iteration inside a workspace after ma_muon_step (for inspection; valid
+ * until the workspace is reused; with MA_EQ_ROWS_POST the row scaling is
+ * applied later, in the update, and is not included). *u receives a DEVICE
+ * pointer into `workspace`, in the parameter's layout (rows x cols, row pitch
+ * *ld elements); *transposed (may be null) is set to 0; *elem_bytes is 2
+ * (bf16 iteration) or 4 (fp32). */
+int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups,
+                             const ma_muon_hparams* hp, void* workspace, int32_t group,
+                             int32_t index, void** u, int64_t* ld, int32_t* transposed,
+                             int32_t* elem_bytes);
+
+/* One flat AdamW buffer. param, grad, exp_avg, exp_avg_sq: DEVICE pointers to
+ * n elements each (fp32; param_dtype and grad_dtype must be MA_F32). `step` is
+ * the 1-based step count after increment (1 on the first call). */
+typedef struct {
+  void* param;
+  const void* grad;
+  void* exp_avg;
+  void* exp_avg_sq;
+  int64_t n;
+  int32_t param_dtype, grad_dtype;
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} ma_adamw_segment;
+
+/* One AdamW step over every segment (fp32 throughout), per element:
+ *   p = p*(1 - lr*wd)            (only when wd != 0)
+ *   m = beta1*m + (1-beta1)*g
+ *   v = beta2*v + (1-beta2)*(g*g)
+ *   p = p - (lr/(1-beta1^t)) * (m / (sqrt(v)/sqrt(1-beta2^t) + eps))
+ * Step-dependent scalars are formed in fp64 on the host and rounded to fp32
+ * once; each per-element operation is one correctly rounded fp32 operation
+ * (no fused multiply-add). Segments may be in any order and of any length
+ * (n >= 0); buffers of different segments must not overlap.
+ * `segments` is a HOST array. */
+int ma_adamw_step(const ma_adamw_segment* segments, int32_t n_segments, void* stream);
+
+/* Status text for a code, and the calling thread's last error message. */
+const char* ma_status_string(int status);
+const char* ma_last_error(void);
+
+/* Library version string, and the GPU architecture it was built for. */
+const char* ma_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing. Between ma_profile_begin and ma_profile_end every kernel the
+ * library launches is bracketed by two HIP events recorded on its stream
+ * (host-side objects from a pool of 2*max_launches events created by
+ * ma_profile_begin; no device memory). ma_profile_read synchronises on the
+ * recorded events and returns, for one kernel kind, the summed duration in
+ * milliseconds and the number of launches. Launches beyond max_launches are
+ * not timed. Not thread-safe with concurrent library calls.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  MA_K_ROWNORM = 0,   /* row sums of squares (momentum look-ahead or update) */
+  MA_K_FINALIZE = 1,  /* per-matrix Frobenius / MuonEq factors */
+  MA_K_PRE = 2,       /* momentum update and X0 in both layouts */
+  MA_K_GRAM = 3,      /* A = X X^T */
+  MA_K_POLY = 4,      /* B = b A + c A A */
+  MA_K_AXPY = 5,      /* X' = a X + B X */
+  MA_K_POST = 6,      /* cautious decay and the update */
+  MA_K_ADAMW = 7,
+  MA_K_COUNT = 8
+} ma_kernel_kind;
+
+int ma_profile_begin(int32_t max_launches);
+int ma_profile_end(void);
+int ma_profile_read(int32_t kind, double* total_ms, int64_t* launches);
+
+/* ---------------------------------------------------------------------------
+ * Stage entry points, used by the test suite to check single stages with
+ * identical inputs on both sides. Same conventions as above.
+ * ------------------------------------------------------------------------- */
+
+/* out[i] = bf16 bits of in[i], round to nearest even (DEVICE buffers). */
+int ma_test_bf16_round(const float* in, uint16_t* out, int64_t n, void* stream);
+
+/* Momentum stage alone for one group: M <- RNE(beta*M + G) and, in
+ * mt_out (DEVICE, count*rows*cols fp32, W's layout), the look-ahead
+ * G + beta*m1 (or m1 when nesterov == 0), exactly as ma_muon_step forms it. */
+int ma_test_muon_momentum(const ma_muon_group* group, float beta, int32_t nesterov,
+                          float* mt_out, void* stream);
+
+/* Decay-and-update stage alone for one group: W <- RNE(post(W, U)) with
+ * U (DEVICE, count dense rows x cols matrices of u_dtype, W's layout) and the
+ * scalars c_lr = lr_eff, c_wd = lr_eff*wd passed as they are. Only params[]
+ * of the group is used. decay == 0 skips the decay term. */
+int ma_test_muon_update(const ma_muon_group* group, const void* u, int32_t u_dtype,
+                        float c_lr, float c_wd, int32_t cautious, int32_t decay, void* stream);
+
+/* Newton-Schulz iteration alone: `count` dense m x n matrices (m <= n) in
+ * x0 (DEVICE, dtype `precision`), result in u (DEVICE, same layout). */
+size_t ma_test_ns_workspace_size(int64_t m, int64_t n, int32_t count, int32_t precision);
+int ma_test_ns(int64_t m, int64_t n, int32_t count, int32_t precision, const void* x0, void* u,
+               const float* abc, int32_t ns_steps, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_ADAMW_H */

@@ -204,7 +204,8 @@ def muon_step(W, G, M, *, lr: float, momentum: float = 0.95, nesterov: bool = Tr
     Inputs are arrays holding the stored values (bf16 values as float32).
     Returns a dict with the stored new weight ``W`` and buffer ``M``, the
     update direction ``U`` the decay and update consumed (binary32, param
-    layout), ``X0`` (float64), the mask and the binary32 scalars used.
+    layout), ``U_ns`` the Newton-Schulz result before any MuonEq POST row
+    scaling, ``X0`` (float64), the mask and the binary32 scalars used.
     """
     W = np.asarray(W, dtype=f32)
     R, C = W.shape
@@ -212,6 +213,7 @@ def muon_step(W, G, M, *, lr: float, momentum: float = 0.95, nesterov: bool = Tr
     M_new = _store(m1, mom_dtype)
     x0 = normalize(mt, "pre" if equilibrate == "pre" else "off", norm_eps, eq_eps)
     U = newton_schulz(x0, coeffs, precision, ns_steps)
+    U_ns = np.asarray(U, dtype=f32)
     if equilibrate == "post":
         Uf = np.asarray(U, dtype=f64)
         rho = math.sqrt(float(np.sum(Uf * Uf))) / math.sqrt(R)
@@ -221,7 +223,7 @@ def muon_step(W, G, M, *, lr: float, momentum: float = 0.95, nesterov: bool = Tr
     lr_eff = lr * (lr_multiplier(R, C) if lr_scale else 1.0)
     c_lr, c_wd = f32(lr_eff), f32(lr_eff * weight_decay)
     w2, mask = post_stage(W, u, c_lr, c_wd, cautious, decay=(weight_decay != 0.0))
-    return {"W": _store(w2, param_dtype), "M": M_new, "U": u, "X0": x0, "mask": mask,
+    return {"W": _store(w2, param_dtype), "M": M_new, "U": u, "U_ns": U_ns, "X0": x0, "mask": mask,
             "c_lr": c_lr, "c_wd": c_wd, "m1": m1, "mt": mt}
 
 
