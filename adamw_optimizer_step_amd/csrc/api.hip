@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -62,8 +64,24 @@ inline int64_t dt_bytes(int dt) { return dt == MA_BF16 ? 2 : 4; }
 inline bool dt_valid(int dt) { return dt == MA_F32 || dt == MA_BF16; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr NsTile kTileBf16 = {128, 128, 64};
-constexpr NsTile kTileF32 = {128, 128, 32};
+// Newton-Schulz GEMM tiles. The symmetric products (Gram, polynomial) need
+// square tiles; MA_NS_TILE / MA_NS_TILE_SYM ("BMxBNxBK:WGMxWGN") override the
+// bf16 choices for tuning.
+NsTile parse_tile(const char* env, NsTile d) {
+  if (const char* e = getenv(env)) {
+    if (strcmp(e, "dma") == 0) return {256, 256, 32, 2, 2, 1};
+    NsTile x{};
+    if (sscanf(e, "%dx%dx%d:%dx%d", &x.bm, &x.bn, &x.bk, &x.wgm, &x.wgn) == 5) return x;
+  }
+  return d;
+}
+
+NsTile ns_tile(int dtype, bool symmetric) {
+  if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
+  static const NsTile axpy = parse_tile("MA_NS_TILE", {256, 256, 32, 2, 2, 1});
+  static const NsTile sym = parse_tile("MA_NS_TILE_SYM", {256, 256, 32, 2, 2, 1});
+  return symmetric ? sym : axpy;
+}
 
 // ----------------------------------------------------------------------------
 // plan of one Muon call
@@ -239,7 +257,6 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
 int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
                hipStream_t s) {
   if (T == 0 || plan.g.empty()) return MA_OK;
-  const NsTile tile = dtype == MA_BF16 ? kTileBf16 : kTileF32;
   // groups with the most work per tile first (they set the tail of a launch)
   std::vector<int> order;
   for (int i = 0; i < (int)plan.g.size(); ++i)
@@ -250,20 +267,21 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
     const int cur = step & 1, nxt = cur ^ 1;
     const bool last = step == T - 1;
     for (int epi = EPI_GRAM; epi <= EPI_AXPY; ++epi) {
+      const NsTile tile = ns_tile(dtype, epi != EPI_AXPY);
+      if (epi != EPI_AXPY && tile.bm != tile.bn) return fail(MA_ERR_INVALID_ARG, "symmetric GEMM tile must be square");
       for (size_t base = 0; base < order.size(); base += kMaxNsGroups) {
         NsArgs A{};
         A.a = abc[3 * step];
         A.b = abc[3 * step + 1];
         A.c = abc[3 * step + 2];
-        int jobs = 0;
         const size_t nb = std::min(order.size() - base, (size_t)kMaxNsGroups);
+        int rot = 0;
         for (size_t q = 0; q < nb; ++q) {
           const GroupPlan& p = plan.g[order[base + q]];
           NsGroup& G = A.g[q];
           const int tm = (int)(p.m_pad / tile.bm);
           const int tn = (int)(p.n_pad / tile.bn);
           G.count = p.count;
-          G.block_begin = jobs;
           if (epi == EPI_GRAM || epi == EPI_POLY) {
             const unsigned char* src = ws + (epi == EPI_GRAM ? p.off_x[cur] : p.off_a);
             G.P = G.Q = src;
@@ -302,12 +320,25 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.tiles = tm * tn;
             G.symmetric = 0;
           }
-          jobs += G.count * G.tiles;
+          G.unit = G.count >= 8 ? G.tiles : 1;
+          G.rot = rot;
+          rot = (rot + G.count * G.tiles / G.unit) & 7;
         }
         (void)e;
         A.n_groups = (int32_t)nb;
-        A.total_jobs = jobs;
-        A.padded_blocks = (jobs + 7) / 8 * 8;
+        int per_xcd = 0;
+        for (int x = 0; x < 8; ++x) {
+          int jx = 0;
+          for (size_t q = 0; q < nb; ++q) {
+            const NsGroup& G = A.g[q];
+            const int units = G.count * G.tiles / G.unit;
+            const int u0 = (x - G.rot + 8) & 7;
+            jx += (units > u0 ? (units - u0 + 7) / 8 : 0) * G.unit;
+          }
+          per_xcd = std::max(per_xcd, jx);
+        }
+        A.per_xcd = per_xcd;
+        A.padded_blocks = 8 * per_xcd;
         hipError_t err;
         {
           ProfScope ps(MA_K_GRAM + epi, s);

@@ -12,14 +12,17 @@
 // The epilogues fuse the a/b/c combination and the mirrored or dual-layout
 // stores, staged through LDS so that global stores are 16-byte coalesced.
 //
-// Kernel shape: 256 threads = 4 waves in a 2x2 grid; each wave owns a
-// (BM/2) x (BN/2) sub-tile made of 32x32 MFMA blocks (bf16:
-// v_mfma_f32_32x32x16_bf16, fp32: v_mfma_f32_32x32x2_f32). P and Q tiles of
-// BM x BK and BN x BK are double-buffered in LDS with a 16-byte row pad
-// (conflict-free 16-byte fragment reads); global loads of the next K tile
-// are issued before the MFMAs of the current one. The block index is
-// remapped so that each of the 8 XCDs walks a contiguous run of tiles (tiles
-// of one matrix share its L2).
+// Two kernels share the job mapping and the epilogue:
+//  * ns_gemm_dma (bf16): 256 x 256 block tile, 4 waves of 128 x 128 (32x32x16
+//    MFMAs, 16 accumulator blocks per wave). Operand tiles of 256 x 32 move
+//    from global memory straight into a 3-stage LDS ring with
+//    global_load_lds_dwordx4 (no VGPR staging), two tiles ahead of the one
+//    being multiplied; 16-byte chunks are XOR-swizzled by row so that the
+//    fragment reads are conflict-free.
+//  * ns_gemm_reg (fp32, and bf16 for small matrices): a register-staged
+//    double-buffered kernel of configurable tile and wave layout.
+// Blocks are dealt to the 8 XCDs so that each XCD gets an eighth of every
+// shape group, whole matrices at a time where possible (see NsArgs).
 #include "ns_gemm.hpp"
 
 namespace ma {
@@ -45,187 +48,130 @@ template <> struct MfmaTraits<DT_F32> {
 // its operand; both operands use the same slot-to-k assignment, so the sum
 // over the slice is complete whatever order the unit adds the slots in.
 template <int DT>
-__device__ __forceinline__ void mfma_frag(f32x16_t& acc, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mfma_frag(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
   if constexpr (DT == DT_BF16) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   } else {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
   }
 }
 
-template <int DT, int BM, int BN, int BK>
-struct NsSmem {
-  using Tr = MfmaTraits<DT>;
-  static constexpr int LDK = BK + Tr::kPad;
-  static constexpr int STAGE = (BM + BN) * LDK;
-  static constexpr int MAIN = 2 * STAGE * Tr::kElem;
-  static constexpr int LDT = BM + Tr::kPad;   // staging S_T[BN][LDT]: rows j, contiguous i
-  static constexpr int LDN = BN + Tr::kPad;   // staging S_N[BM][LDN]: rows i, contiguous j
-  static constexpr int EPI = (BN * LDT > BM * LDN ? BN * LDT : BM * LDN) * Tr::kElem;
-  static constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
+// ---------------------------------------------------------------------------
+// job -> (group, matrix, tile)
+// ---------------------------------------------------------------------------
+struct TileJob {
+  int gi, mat, bi, bj;
 };
 
-template <int DT, int EPI, int BM, int BN, int BK>
-__global__ void __launch_bounds__(256) ns_gemm_kernel(const NsArgs args) {
+__device__ __forceinline__ bool map_job(const NsArgs& args, TileJob& J) {
+  const int x = (int)(blockIdx.x & 7);
+  int local = (int)(blockIdx.x >> 3);
+  // walk the groups in order; XCD x owns units u0, u0+8, ... of each, where
+  // u0 = (x - rot) mod 8
+#pragma unroll
+  for (int q = 0; q < kMaxNsGroups; ++q) {
+    if (q >= args.n_groups) return false;
+    const NsGroup& G = args.g[q];
+    const int units = G.count * G.tiles / G.unit;
+    const int u0 = (x - G.rot + 8) & 7;
+    const int mine = units > u0 ? (units - u0 + 7) / 8 : 0;
+    const int njobs = mine * G.unit;
+    if (local < njobs) {
+      const int unit = u0 + 8 * (local / G.unit);
+      const int gjob = unit * G.unit + local % G.unit;
+      const int mat = gjob / G.tiles;
+      int t = gjob - mat * G.tiles;
+      int bi, bj;
+      if (G.symmetric) {
+        bi = 0;
+        int len = G.tm;
+        while (t >= len) { t -= len; ++bi; --len; }
+        bj = bi + t;
+      } else {
+        bi = t / G.tn;
+        bj = t - bi * G.tn;
+      }
+      J.gi = q;
+      J.mat = mat;
+      J.bi = bi;
+      J.bj = bj;
+      return true;
+    }
+    local -= njobs;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// epilogue: a/b/c combination, then staged, coalesced stores
+// ---------------------------------------------------------------------------
+template <int DT, int BM, int BN>
+struct EpiSmem {
+  using Tr = MfmaTraits<DT>;
+  static constexpr int LDT = BM + Tr::kPad;   // staging S_T[BN][LDT]: rows j, contiguous i
+  static constexpr int LDN = BN + Tr::kPad;   // staging S_N[BM][LDN]: rows i, contiguous j
+  static constexpr int BYTES = (BN * LDT > BM * LDN ? BN * LDT : BM * LDN) * Tr::kElem;
+};
+
+// Accumulator layout of a 32x32 MFMA block: lane l holds column (l % 32) and,
+// in registers 4q..4q+3, rows 8q + 4(l/32) + 0..3. The caller has finished
+// with LDS (a barrier precedes the call).
+template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false>
+__device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
+                                            f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                            unsigned char* smem) {
   using Tr = MfmaTraits<DT>;
   using T = typename Tr::T;
-  using SM = NsSmem<DT, BM, BN, BK>;
-  constexpr int LDK = SM::LDK;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  using ES = EpiSmem<DT, BM, BN>;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int VEC = 16 / Tr::kElem;     // elements per 16-byte vector
-  constexpr int VPR = BK / VEC;           // vectors per tile row
-  constexpr int PV = BM * VPR / 256;
-  constexpr int QV = BN * VPR / 256;
-  static_assert(BM * VPR % 256 == 0 && BN * VPR % 256 == 0, "tile/thread mismatch");
-  static_assert(BK % Tr::kFragK == 0, "BK");
-  static_assert(FM >= 1 && FN >= 1, "wave tile");
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
-
-  // ---- job -> (group, matrix, tile) ---------------------------------------
-  const int per_xcd = args.padded_blocks >> 3;
-  const int job = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (job >= args.total_jobs) return;
-  int gi = 0;
-#pragma unroll
-  for (int q = 1; q < kMaxNsGroups; ++q)
-    if (q < args.n_groups && job >= args.g[q].block_begin) gi = q;
-  const NsGroup& G = args.g[gi];
-  const int local = job - G.block_begin;
-  const int mat = local / G.tiles;
-  int t = local - mat * G.tiles;
-  int bi, bj;
-  if (G.symmetric) {
-    bi = 0;
-    int len = G.tm;
-    while (t >= len) { t -= len; ++bi; --len; }
-    bj = bi + t;
-  } else {
-    bi = t / G.tn;
-    bj = t - bi * G.tn;
-  }
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int VEC = 16 / Tr::kElem;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, lh = lane >> 5;
-
-  const T* __restrict__ Pg = reinterpret_cast<const T*>(G.P) + (int64_t)mat * G.sP + (int64_t)bi * BM * G.ldP;
-  const T* __restrict__ Qg = reinterpret_cast<const T*>(G.Q) + (int64_t)mat * G.sQ + (int64_t)bj * BN * G.ldQ;
-  const int ldP = G.ldP, ldQ = G.ldQ;
-
-  T* sbase = reinterpret_cast<T*>(smem);
-
-  uint4 rp[PV], rq[QV];
-#define MA_NS_GLOAD(k0)                                                                   \
-  do {                                                                                    \
-    _Pragma("unroll") for (int v = 0; v < PV; ++v) {                                      \
-      const int idx_ = tid + 256 * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                \
-      rp[v] = *reinterpret_cast<const uint4*>(Pg + (int64_t)row_ * ldP + (k0) + ch_ * VEC); \
-    }                                                                                     \
-    _Pragma("unroll") for (int v = 0; v < QV; ++v) {                                      \
-      const int idx_ = tid + 256 * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                \
-      rq[v] = *reinterpret_cast<const uint4*>(Qg + (int64_t)row_ * ldQ + (k0) + ch_ * VEC); \
-    }                                                                                     \
-  } while (0)
-#define MA_NS_SSTORE(stage)                                                               \
-  do {                                                                                    \
-    T* sP_ = sbase + (stage) * SM::STAGE;                                                 \
-    T* sQ_ = sP_ + BM * LDK;                                                              \
-    _Pragma("unroll") for (int v = 0; v < PV; ++v) {                                      \
-      const int idx_ = tid + 256 * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                \
-      *reinterpret_cast<uint4*>(sP_ + row_ * LDK + ch_ * VEC) = rp[v];                     \
-    }                                                                                     \
-    _Pragma("unroll") for (int v = 0; v < QV; ++v) {                                      \
-      const int idx_ = tid + 256 * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                \
-      *reinterpret_cast<uint4*>(sQ_ + row_ * LDK + ch_ * VEC) = rq[v];                     \
-    }                                                                                     \
-  } while (0)
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-#define MA_NS_COMPUTE(stage)                                                                  \
-  do {                                                                                        \
-    const T* sP_ = sbase + (stage) * SM::STAGE;                                               \
-    const T* sQ_ = sP_ + BM * LDK;                                                            \
-    _Pragma("unroll") for (int kk = 0; kk < BK / Tr::kFragK; ++kk) {                          \
-      uint4 fa[FM], fb[FN];                                                                   \
-      const int koff = kk * Tr::kFragK + lh * Tr::kLaneK;                                     \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
-        fa[i] = *reinterpret_cast<const uint4*>(sP_ + (wm * WTM + i * 32 + l32) * LDK + koff); \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                          \
-        fb[j] = *reinterpret_cast<const uint4*>(sQ_ + (wn * WTN + j * 32 + l32) * LDK + koff); \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j) mfma_frag<DT>(acc[i][j], fa[i], fb[j]); \
-    }                                                                                         \
-  } while (0)
-
-  const int nk = G.K / BK;
-  MA_NS_GLOAD(0);
-  MA_NS_SSTORE(0);
-  __syncthreads();
-  int cur = 0;
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    MA_NS_GLOAD((kt + 1) * BK);
-    MA_NS_COMPUTE(cur);
-    MA_NS_SSTORE(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-  }
-  MA_NS_COMPUTE(cur);
-  __syncthreads();   // every wave is done with the operand tiles; LDS is reused below
-#undef MA_NS_GLOAD
-#undef MA_NS_COMPUTE
-#undef MA_NS_SSTORE
-
-  // ---- epilogue ------------------------------------------------------------
-  // Accumulator layout of a 32x32 MFMA block: lane l holds column (l % 32)
-  // and, in registers 4q..4q+3, rows 8q + 4(l/32) + 0..3.
+  const int mat = J.mat, bi = J.bi, bj = J.bj;
   const bool diag = G.symmetric && bi == bj;
   T* outT = reinterpret_cast<T*>(G.outT);
   T* outN = diag ? nullptr : reinterpret_cast<T*>(G.outN);
 
-  if constexpr (EPI != EPI_GRAM) {
-    // E[j][i..i+3]: A (symmetric) for POLY, X^T for AXPY
+  if constexpr (EPI != EPI_GRAM && !E_DONE) {
+    // E[j][i..i+3]: A (symmetric) for POLY, X^T for AXPY; one 32x32 block at
+    // a time, so that the loads of all blocks are not held in registers at once
     const T* Eg = reinterpret_cast<const T*>(G.E) + (int64_t)mat * G.sE;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int jl = wn * WTN + j * 32 + l32;
+        float e[4][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int il = wm * WTM + i * 32 + q * 8 + lh * 4;
           const T* ep = Eg + (int64_t)(bj * BN + jl) * G.ldE + bi * BM + il;
-          float e[4];
           if constexpr (DT == DT_BF16) {
             const uint2 u = *reinterpret_cast<const uint2*>(ep);
-            e[0] = __uint_as_float(u.x << 16); e[1] = __uint_as_float(u.x & 0xFFFF0000u);
-            e[2] = __uint_as_float(u.y << 16); e[3] = __uint_as_float(u.y & 0xFFFF0000u);
+            e[q][0] = __uint_as_float(u.x << 16); e[q][1] = __uint_as_float(u.x & 0xFFFF0000u);
+            e[q][2] = __uint_as_float(u.y << 16); e[q][3] = __uint_as_float(u.y & 0xFFFF0000u);
           } else {
             const float4 u = *reinterpret_cast<const float4*>(ep);
-            e[0] = u.x; e[1] = u.y; e[2] = u.z; e[3] = u.w;
+            e[q][0] = u.x; e[q][1] = u.y; e[q][2] = u.z; e[q][3] = u.w;
           }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if constexpr (EPI == EPI_POLY)
-              acc[i][j][4 * q + r] = __builtin_fmaf(args.b, e[r], args.c * acc[i][j][4 * q + r]);
+              acc[i][j][4 * q + r] = __builtin_fmaf(args.b, e[q][r], args.c * acc[i][j][4 * q + r]);
             else
-              acc[i][j][4 * q + r] = __builtin_fmaf(args.a, e[r], acc[i][j][4 * q + r]);
+              acc[i][j][4 * q + r] = __builtin_fmaf(args.a, e[q][r], acc[i][j][4 * q + r]);
           }
-        }
+        asm volatile("" ::: "memory");
       }
   }
 
@@ -244,9 +190,9 @@ __global__ void __launch_bounds__(256) ns_gemm_kernel(const NsArgs args) {
             uint2 u;
             u.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
             u.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *reinterpret_cast<uint2*>(stg + jl * SM::LDT + il) = u;
+            *reinterpret_cast<uint2*>(stg + jl * ES::LDT + il) = u;
           } else {
-            *reinterpret_cast<float4*>(stg + jl * SM::LDT + il) =
+            *reinterpret_cast<float4*>(stg + jl * ES::LDT + il) =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           }
         }
@@ -255,10 +201,10 @@ __global__ void __launch_bounds__(256) ns_gemm_kernel(const NsArgs args) {
     T* dst = outT + (int64_t)mat * G.sT + (int64_t)(bj * BN) * G.ldT + bi * BM;
     constexpr int CPR = BM / VEC;   // 16-byte chunks per staged row
 #pragma unroll
-    for (int u = 0; u < BN * CPR / 256; ++u) {
-      const int idx = tid + 256 * u, r = idx / CPR, ch = idx % CPR;
+    for (int u = 0; u < BN * CPR / NT; ++u) {
+      const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
       *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldT + ch * VEC) =
-          *reinterpret_cast<const uint4*>(stg + r * SM::LDT + ch * VEC);
+          *reinterpret_cast<const uint4*>(stg + r * ES::LDT + ch * VEC);
     }
     if (outN) __syncthreads();
   }
@@ -275,13 +221,13 @@ __global__ void __launch_bounds__(256) ns_gemm_kernel(const NsArgs args) {
           if constexpr (DT == DT_BF16) {
             const uint32_t p01 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
             const uint32_t p23 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            stg[(il + 0) * SM::LDN + jl] = (uint16_t)(p01 & 0xFFFFu);
-            stg[(il + 1) * SM::LDN + jl] = (uint16_t)(p01 >> 16);
-            stg[(il + 2) * SM::LDN + jl] = (uint16_t)(p23 & 0xFFFFu);
-            stg[(il + 3) * SM::LDN + jl] = (uint16_t)(p23 >> 16);
+            stg[(il + 0) * ES::LDN + jl] = (uint16_t)(p01 & 0xFFFFu);
+            stg[(il + 1) * ES::LDN + jl] = (uint16_t)(p01 >> 16);
+            stg[(il + 2) * ES::LDN + jl] = (uint16_t)(p23 & 0xFFFFu);
+            stg[(il + 3) * ES::LDN + jl] = (uint16_t)(p23 >> 16);
           } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) stg[(il + r) * SM::LDN + jl] = acc[i][j][4 * q + r];
+            for (int r = 0; r < 4; ++r) stg[(il + r) * ES::LDN + jl] = acc[i][j][4 * q + r];
           }
         }
       }
@@ -289,39 +235,372 @@ __global__ void __launch_bounds__(256) ns_gemm_kernel(const NsArgs args) {
     T* dst = outN + (int64_t)mat * G.sN + (int64_t)(bi * BM) * G.ldN + bj * BN;
     constexpr int CPR = BN / VEC;
 #pragma unroll
-    for (int u = 0; u < BM * CPR / 256; ++u) {
-      const int idx = tid + 256 * u, r = idx / CPR, ch = idx % CPR;
+    for (int u = 0; u < BM * CPR / NT; ++u) {
+      const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
       *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldN + ch * VEC) =
-          *reinterpret_cast<const uint4*>(stg + r * SM::LDN + ch * VEC);
+          *reinterpret_cast<const uint4*>(stg + r * ES::LDN + ch * VEC);
     }
   }
 }
 
-template <int DT, int EPI, int BM, int BN, int BK>
-static hipError_t launch_one(const NsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((ns_gemm_kernel<DT, EPI, BM, BN, BK>), dim3(a.padded_blocks), dim3(256), 0, s, a);
+// ---------------------------------------------------------------------------
+// register-staged kernel
+// ---------------------------------------------------------------------------
+template <int DT, int BM, int BN, int BK>
+struct RegSmem {
+  using Tr = MfmaTraits<DT>;
+  static constexpr int LDK = BK + Tr::kPad;
+  static constexpr int STAGE = (BM + BN) * LDK;
+  static constexpr int MAIN = 2 * STAGE * Tr::kElem;
+  static constexpr int EPI = EpiSmem<DT, BM, BN>::BYTES;
+  static constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
+};
+
+template <int DT, int EPI, int BM, int BN, int BK, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, 2)))
+ns_gemm_reg(const NsArgs args) {
+  using Tr = MfmaTraits<DT>;
+  using T = typename Tr::T;
+  using SM = RegSmem<DT, BM, BN, BK>;
+  constexpr int NT = 64 * WGM * WGN;      // threads: WGM x WGN waves
+  constexpr int LDK = SM::LDK;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int VEC = 16 / Tr::kElem;     // elements per 16-byte vector
+  constexpr int VPR = BK / VEC;           // vectors per tile row
+  constexpr int PV = BM * VPR / NT;
+  constexpr int QV = BN * VPR / NT;
+  static_assert(BM * VPR % NT == 0 && BN * VPR % NT == 0, "tile/thread mismatch");
+  static_assert(BK % Tr::kFragK == 0, "BK");
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
+  TileJob J;
+  if (!map_job(args, J)) return;
+  const NsGroup& G = args.g[J.gi];
+  const int mat = J.mat, bi = J.bi, bj = J.bj;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  const T* __restrict__ Pg = reinterpret_cast<const T*>(G.P) + (int64_t)mat * G.sP + (int64_t)bi * BM * G.ldP;
+  const T* __restrict__ Qg = reinterpret_cast<const T*>(G.Q) + (int64_t)mat * G.sQ + (int64_t)bj * BN * G.ldQ;
+  const int ldP = G.ldP, ldQ = G.ldQ;
+
+  T* sbase = reinterpret_cast<T*>(smem);
+
+  // two register sets: the global loads of tile k+2 are in flight while tile
+  // k is multiplied and tile k+1 moves from registers to LDS
+  u32x4_t rp0[PV], rq0[QV], rp1[PV], rq1[QV];
+#define MA_NS_GLOAD(RP, RQ, k0)                                                           \
+  do {                                                                                    \
+    _Pragma("unroll") for (int v = 0; v < PV; ++v) {                                      \
+      const int idx_ = tid + NT * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                 \
+      RP[v] = *reinterpret_cast<const u32x4_t*>(Pg + (int64_t)row_ * ldP + (k0) + ch_ * VEC); \
+    }                                                                                     \
+    _Pragma("unroll") for (int v = 0; v < QV; ++v) {                                      \
+      const int idx_ = tid + NT * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                 \
+      RQ[v] = *reinterpret_cast<const u32x4_t*>(Qg + (int64_t)row_ * ldQ + (k0) + ch_ * VEC); \
+    }                                                                                     \
+  } while (0)
+#define MA_NS_SSTORE(RP, RQ, stage)                                                       \
+  do {                                                                                    \
+    T* sP_ = sbase + (stage) * SM::STAGE;                                                 \
+    T* sQ_ = sP_ + BM * LDK;                                                              \
+    _Pragma("unroll") for (int v = 0; v < PV; ++v) {                                      \
+      const int idx_ = tid + NT * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                 \
+      *reinterpret_cast<u32x4_t*>(sP_ + row_ * LDK + ch_ * VEC) = RP[v];                   \
+    }                                                                                     \
+    _Pragma("unroll") for (int v = 0; v < QV; ++v) {                                      \
+      const int idx_ = tid + NT * v, row_ = idx_ / VPR, ch_ = idx_ % VPR;                 \
+      *reinterpret_cast<u32x4_t*>(sQ_ + row_ * LDK + ch_ * VEC) = RQ[v];                   \
+    }                                                                                     \
+  } while (0)
+#define MA_NS_COMPUTE(stage)                                                                  \
+  do {                                                                                        \
+    const T* sP_ = sbase + (stage) * SM::STAGE;                                               \
+    const T* sQ_ = sP_ + BM * LDK;                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < BK / Tr::kFragK; ++kk) {                          \
+      u32x4_t fa[FM], fb[FN];                                                                 \
+      const int koff = kk * Tr::kFragK + lh * Tr::kLaneK;                                     \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+        fa[i] = *reinterpret_cast<const u32x4_t*>(sP_ + (wm * WTM + i * 32 + l32) * LDK + koff); \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                          \
+        fb[j] = *reinterpret_cast<const u32x4_t*>(sQ_ + (wn * WTN + j * 32 + l32) * LDK + koff); \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) mfma_frag<DT>(acc[i][j], fa[i], fb[j]); \
+    }                                                                                         \
+  } while (0)
+// keeps the global loads issued above it from being sunk below it
+#define MA_NS_PIN() asm volatile("" ::: "memory")
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // K is a multiple of 256, so nk >= 2 for every tile configuration used
+  const int nk = G.K / BK;
+  MA_NS_GLOAD(rp0, rq0, 0);
+  MA_NS_GLOAD(rp1, rq1, BK);
+  MA_NS_SSTORE(rp0, rq0, 0);
+  __syncthreads();
+  // steady state, two k-tiles per trip: tile kt uses stage 0 and register set
+  // 0 for its successor's successor, tile kt+1 stage 1 and set 1
+  int kt = 0;
+  for (; kt + 3 < nk; kt += 2) {
+    MA_NS_GLOAD(rp0, rq0, (kt + 2) * BK);
+    MA_NS_PIN();
+    MA_NS_COMPUTE(0);
+    MA_NS_PIN();
+    MA_NS_SSTORE(rp1, rq1, 1);
+    __syncthreads();
+    MA_NS_GLOAD(rp1, rq1, (kt + 3) * BK);
+    MA_NS_PIN();
+    MA_NS_COMPUTE(1);
+    MA_NS_PIN();
+    MA_NS_SSTORE(rp0, rq0, 0);
+    __syncthreads();
+  }
+  // tail: tiles kt .. nk-1 (two or three of them); set 1 holds tile kt+1
+  if (kt + 2 < nk) {        // three left: kt (stage 0), kt+1 (set 1), kt+2 (to load)
+    MA_NS_GLOAD(rp0, rq0, (kt + 2) * BK);
+    MA_NS_PIN();
+    MA_NS_COMPUTE(0);
+    MA_NS_PIN();
+    MA_NS_SSTORE(rp1, rq1, 1);
+    __syncthreads();
+    MA_NS_COMPUTE(1);
+    MA_NS_SSTORE(rp0, rq0, 0);
+    __syncthreads();
+    MA_NS_COMPUTE(0);
+  } else {                  // two left: kt (stage 0), kt+1 (set 1)
+    MA_NS_COMPUTE(0);
+    MA_NS_SSTORE(rp1, rq1, 1);
+    __syncthreads();
+    MA_NS_COMPUTE(1);
+  }
+  __syncthreads();   // every wave is done with the operand tiles; LDS is reused below
+#undef MA_NS_GLOAD
+#undef MA_NS_COMPUTE
+#undef MA_NS_PIN
+#undef MA_NS_SSTORE
+
+  ns_epilogue<DT, EPI, BM, BN, WGM, WGN>(args, G, J, acc, smem);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-DMA kernel (bf16): 256 x 256 x 32 tiles, 4 waves of 128 x 128, 3 stages
+// ---------------------------------------------------------------------------
+namespace dma {
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 3;
+constexpr int ROWB = BK * 2;                      // bytes per tile row (64)
+constexpr int STAGE_BYTES = (BM + BN) * ROWB;     // 32 KiB: P rows 0..255, Q rows 256..511
+constexpr int MAIN = STAGES * STAGE_BYTES;
+constexpr int EPI = EpiSmem<DT_BF16, BM, BN>::BYTES;
+constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
+constexpr int DMA_PER_WAVE = STAGE_BYTES / 4 / 1024;   // 1 KiB per wave instruction: 8
+}  // namespace dma
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+#define MA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// One k-tile: issue this wave's DMA of a later tile into `fill` (when
+// do_fill), then multiply the tile in `cur`. The two stage pointers are
+// distinct (__restrict__), which lets the compiler see that the fragment
+// reads of `cur` do not depend on the DMA into `fill`.
+//
+// e_blk >= 0 (AXPY only): this k-tile's 32 values of k are the rows
+// i_blk = e_blk of this wave's output block, and the Q fragments (X^T rows j)
+// hold X^T[j][i] = X[i][j] for them: the term a*X is added to the fp32
+// accumulators here instead of being read back from memory in the epilogue.
+__device__ __forceinline__ void dma_ktile(const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill,
+                                          bool do_fill, const uint16_t* src, int ld_src, int lane_off,
+                                          int k0, int lane, int wm, int wn, f32x16_t (&acc)[4][4], int e_blk,
+                                          float a_coef) {
+  using namespace dma;
+  if (do_fill) {
+    // this wave fills 8 KiB of the stage: rows [w*128, w*128+128) of P or Q
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q)
+      __builtin_amdgcn_global_load_lds(src + (int64_t)(q * 16) * ld_src + lane_off + k0,
+                                       (lds_void_t*)(fill + q * 1024), 16, 0, 0);
+  }
+  // fragments: row r, logical 16-byte chunk c stored at chunk c ^ ((r >> 2) & 3)
+  const int l32 = lane & 31, lh = lane >> 5;
+  u32x4_t fa[2][4], fb[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = kk * 2 + lh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + l32;
+      fa[kk][i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ ((r >> 2) & 3)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = BM + wn * 128 + j * 32 + l32;
+      fb[kk][j] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ ((r >> 2) & 3)) << 4));
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mfma_frag<DT_BF16>(acc[i][j], fa[kk][i], fb[kk][j]);
+  if (e_blk >= 0) {
+    // acc[e_blk][j] += (a I) X^T-block: one more MFMA per fragment step with
+    // an identity A operand (a split as a_hi + a_lo, both exact in bf16) and
+    // the X^T fragment already in registers: lane (l32, lh) holds k =
+    // 16 kk + 8 lh + e, and row i = l32 of a I is nonzero only at k = i.
+    const float a_hi = __builtin_bit_cast(float, __float_as_uint(a_coef) & 0xFFFF0000u);
+    const float a_lo = a_coef - a_hi;
+    const uint32_t hi16 = __float_as_uint(a_hi) >> 16;
+    const uint32_t lo16 = pack_bf16x2(a_lo, 0.0f) & 0xFFFFu;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int e = l32 - 16 * kk - 8 * lh;   // the lane's nonzero slot, if in 0..7
+      u32x4_t id_hi = {0u, 0u, 0u, 0u}, id_lo = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        id_hi[w] = (e == 2 * w ? hi16 : 0u) | (e == 2 * w + 1 ? hi16 << 16 : 0u);
+        id_lo[w] = (e == 2 * w ? lo16 : 0u) | (e == 2 * w + 1 ? lo16 << 16 : 0u);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        if (ii != e_blk) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mfma_frag<DT_BF16>(acc[ii][j], id_hi, fb[kk][j]);
+          mfma_frag<DT_BF16>(acc[ii][j], id_lo, fb[kk][j]);
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ns_gemm_dma(const NsArgs args) {
+  using namespace dma;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES];
+  TileJob J;
+  if (!map_job(args, J)) return;
+  const NsGroup& G = args.g[J.gi];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // DMA source of this wave: waves 0,1 load P rows [w*128, +128), waves 2,3
+  // Q rows [(w-2)*128, +128). Lane i of instruction q lands in the stage at
+  // byte (w*8 + q)*1024 + 16 i, i.e. tile row (w*8+q)*16 + i/4 (P and Q rows
+  // are contiguous), physical chunk i%4 holding logical chunk
+  // (i%4) ^ ((row >> 2) & 3) = (i%4) ^ ((i/16) & 3). With 64-byte rows, the
+  // 16 lanes an LDS cycle serves (rows r..r+15 of one chunk column) then hit
+  // 16 distinct 16-byte bank groups.
+  const bool isP = wave < 2;
+  const int ld_src = isP ? G.ldP : G.ldQ;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) +
+                        (int64_t)J.mat * (isP ? G.sP : G.sQ) +
+                        (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave & 1) * 128) * ld_src;
+  const int lane_off = (lane >> 2) * ld_src + (((lane & 3) ^ ((lane >> 4) & 3)) << 3);
+  unsigned char* wave_fill = smem + wave * (DMA_PER_WAVE * 1024);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = G.K / BK;   // K is a multiple of 256: nk >= 8
+  // prologue: tiles 0 and 1 into stages 0 and 1
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q)
+      __builtin_amdgcn_global_load_lds(src + (int64_t)(q * 16) * ld_src + lane_off + t * BK,
+                                       (lds_void_t*)(wave_fill + t * STAGE_BYTES + q * 1024), 16, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed for this wave once at most the DMA of tile kt+1 is
+    // outstanding; the barrier makes that true for every wave, and also
+    // guarantees every wave is done reading the stage the next DMA refills
+    if (kt + 1 < nk) MA_WAIT_VMCNT(dma::DMA_PER_WAVE);
+    else MA_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    const int s_cur = kt % STAGES, s_fill = (kt + 2) % STAGES;
+    int e_blk = -1;
+    if constexpr (EPI == EPI_AXPY) {
+      const int d = kt * BK - (J.bi * BM + wm * 128);
+      if (d >= 0 && d < 128) e_blk = d >> 5;
+    }
+    dma_ktile(smem + s_cur * STAGE_BYTES, wave_fill + s_fill * STAGE_BYTES, kt + 2 < nk, src, ld_src, lane_off,
+              (kt + 2) * BK, lane, wm, wn, acc, e_blk, args.a);
+  }
+  __syncthreads();   // operand tiles no longer needed; LDS is reused below
+  ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, EPI == EPI_AXPY>(args, G, J, acc, smem);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int DT, int EPI, int BM, int BN, int BK, int WGM, int WGN>
+static hipError_t launch_reg(const NsArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((ns_gemm_reg<DT, EPI, BM, BN, BK, WGM, WGN>), dim3(a.padded_blocks), dim3(64 * WGM * WGN),
+                     0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int BM, int BN, int BK>
-static hipError_t launch_epi(int epi, const NsArgs& a, hipStream_t s) {
+template <int DT, int BM, int BN, int BK, int WGM, int WGN>
+static hipError_t launch_reg_epi(int epi, const NsArgs& a, hipStream_t s) {
   switch (epi) {
-    case EPI_GRAM: return launch_one<DT, EPI_GRAM, BM, BN, BK>(a, s);
-    case EPI_POLY: return launch_one<DT, EPI_POLY, BM, BN, BK>(a, s);
-    case EPI_AXPY: return launch_one<DT, EPI_AXPY, BM, BN, BK>(a, s);
+    case EPI_GRAM: return launch_reg<DT, EPI_GRAM, BM, BN, BK, WGM, WGN>(a, s);
+    case EPI_POLY: return launch_reg<DT, EPI_POLY, BM, BN, BK, WGM, WGN>(a, s);
+    case EPI_AXPY: return launch_reg<DT, EPI_AXPY, BM, BN, BK, WGM, WGN>(a, s);
   }
   return hipErrorInvalidValue;
 }
+
+template <int EPI>
+static hipError_t launch_dma(const NsArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((ns_gemm_dma<EPI>), dim3(a.padded_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+#define MA_NS_TILE(BM_, BN_, BK_, WGM_, WGN_)                                                      \
+  if (tile.bm == BM_ && tile.bn == BN_ && tile.bk == BK_ && tile.wgm == WGM_ && tile.wgn == WGN_) \
+    return launch_reg_epi<DTv, BM_, BN_, BK_, WGM_, WGN_>(epi, a, s);
 
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipStream_t s) {
   if (a.padded_blocks <= 0) return hipSuccess;
   if (dtype == DT_BF16) {
-    if (tile.bm == 128 && tile.bn == 128 && tile.bk == 64) return launch_epi<DT_BF16, 128, 128, 64>(epi, a, s);
-    if (tile.bm == 256 && tile.bn == 256 && tile.bk == 64) return launch_epi<DT_BF16, 256, 256, 64>(epi, a, s);
+    if (tile.dma) {
+      if (tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK) return hipErrorInvalidValue;
+      switch (epi) {
+        case EPI_GRAM: return launch_dma<EPI_GRAM>(a, s);
+        case EPI_POLY: return launch_dma<EPI_POLY>(a, s);
+        case EPI_AXPY: return launch_dma<EPI_AXPY>(a, s);
+      }
+      return hipErrorInvalidValue;
+    }
+    constexpr int DTv = DT_BF16;
+    MA_NS_TILE(128, 128, 64, 2, 2)
   } else {
-    if (tile.bm == 128 && tile.bn == 128 && tile.bk == 32) return launch_epi<DT_F32, 128, 128, 32>(epi, a, s);
+    constexpr int DTv = DT_F32;
+    MA_NS_TILE(128, 128, 32, 2, 2)
   }
   return hipErrorInvalidValue;
 }
+#undef MA_NS_TILE
 
 }  // namespace ma

@@ -28,20 +28,29 @@ struct NsGroup {
   int32_t tm, tn;   // output tile grid
   int32_t tiles;    // tiles per matrix
   int32_t count;
-  int32_t block_begin;
+  int32_t unit;       // jobs per scheduling unit: tiles (whole matrix) or 1 (one tile)
+  int32_t rot;        // unit u of this group goes to XCD (u + rot) % 8
   int32_t symmetric;  // 1: only tiles bi <= bj, mirrored through outN/outT
 };
 
+// Scheduling: the hardware deals consecutive workgroups round-robin to the 8
+// XCDs, so block b runs on XCD b % 8 as its (b / 8)-th block there. Each
+// group's jobs are cut into units (a whole matrix when the group has at least
+// 8 matrices, else single tiles); unit u goes to XCD (u + rot) % 8. Every XCD then
+// gets one eighth of every group (balanced when groups differ in K) and, for
+// whole-matrix units, all tiles of a matrix share one L2. Each group's first
+// unit goes to the XCD after the previous group's last one.
 struct NsArgs {
   int32_t n_groups;
-  int32_t total_jobs;
-  int32_t padded_blocks;   // multiple of 8 (XCD round-robin remap)
+  int32_t per_xcd;         // blocks per XCD (max over XCDs of their job count)
+  int32_t padded_blocks;   // 8 * per_xcd
   float a, b, c;
   NsGroup g[kMaxNsGroups];
 };
 
-// tile configuration chosen per launch
-struct NsTile { int bm, bn, bk; };
+// tile configuration chosen per launch: block tile bm x bn, K tile bk,
+// wgm x wgn waves; dma selects the LDS-DMA kernel (bf16, 256 x 256 x 32)
+struct NsTile { int bm, bn, bk, wgm, wgn, dma; };
 
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& args, hipStream_t s);
 
