@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--no-profile", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the timed steps, run 3 plain device copies of MIB MiB (read MIB, write MIB) "
+                         "as the known-size reference that scales HBM byte counters")
     return ap.parse_args()
 
 
@@ -113,6 +116,17 @@ def main():
         step(i)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 18          # fp32 elements in MIB MiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)              # one elementwise kernel: 4n bytes read, 4n written
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {4 * n} bytes read + {4 * n} written", file=sys.stderr, flush=True)
+        del src, dst
 
     lib = L.lib()
     profile = not args.no_profile
@@ -198,19 +212,20 @@ def main():
 
 
 def traffic_for(kernel, workload_name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading), if every
+    source it was taken on is unchanged; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path))
         import hashlib
-        src = os.path.join(ROOT, rec["source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
-            return None
+        rec = json.load(open(path))
+        for src, digest in rec["sources"].items():
+            if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != digest:
+                return None
         return rec["bytes_per_launch"]
-    except Exception:
+    except (OSError, KeyError, ValueError):
         return None
 
 
