@@ -69,7 +69,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // bf16 choices for tuning.
 NsTile parse_tile(const char* env, NsTile d) {
   if (const char* e = getenv(env)) {
-    if (strcmp(e, "dma") == 0) return {256, 256, 32, 2, 2, 1};
+    if (strcmp(e, "dma") == 0) return {256, 256, ns_dma_bk(), 2, 2, 1};
     NsTile x{};
     if (sscanf(e, "%dx%dx%d:%dx%d", &x.bm, &x.bn, &x.bk, &x.wgm, &x.wgn) == 5) return x;
   }
@@ -78,8 +78,8 @@ NsTile parse_tile(const char* env, NsTile d) {
 
 NsTile ns_tile(int dtype, bool symmetric) {
   if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
-  static const NsTile axpy = parse_tile("MA_NS_TILE", {256, 256, 32, 2, 2, 1});
-  static const NsTile sym = parse_tile("MA_NS_TILE_SYM", {256, 256, 32, 2, 2, 1});
+  static const NsTile axpy = parse_tile("MA_NS_TILE", {256, 256, ns_dma_bk(), 2, 2, 1});
+  static const NsTile sym = parse_tile("MA_NS_TILE_SYM", {256, 256, ns_dma_bk(), 2, 2, 1});
   return symmetric ? sym : axpy;
 }
 

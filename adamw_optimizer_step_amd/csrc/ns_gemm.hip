@@ -396,16 +396,35 @@ ns_gemm_reg(const NsArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-DMA kernel (bf16): 256 x 256 x 32 tiles, 4 waves of 128 x 128, 3 stages
+// LDS-DMA kernel (bf16): 256 x 256 x 32 tiles, 4 waves of 128 x 128, a ring of
+// STAGES k-tiles in LDS
 // ---------------------------------------------------------------------------
+#ifndef MA_DMA_BK
+#define MA_DMA_BK 64
+#endif
+#ifndef MA_DMA_STAGES
+#define MA_DMA_STAGES (MA_DMA_BK == 64 ? 2 : 3)
+#endif
 namespace dma {
-constexpr int BM = 256, BN = 256, BK = 32, STAGES = 3;
-constexpr int ROWB = BK * 2;                      // bytes per tile row (64)
-constexpr int STAGE_BYTES = (BM + BN) * ROWB;     // 32 KiB: P rows 0..255, Q rows 256..511
+constexpr int BM = 256, BN = 256, BK = MA_DMA_BK, STAGES = MA_DMA_STAGES;
+constexpr int ROWB = BK * 2;                      // bytes per tile row
+constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
+constexpr int RPI = 1024 / ROWB;                  // rows per 1 KiB DMA instruction
+constexpr int KK = BK / 16;                       // MFMA k-steps per k-tile
+constexpr int STAGE_BYTES = (BM + BN) * ROWB;     // P rows 0..255, Q rows 256..511
 constexpr int MAIN = STAGES * STAGE_BYTES;
 constexpr int EPI = EpiSmem<DT_BF16, BM, BN>::BYTES;
 constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
-constexpr int DMA_PER_WAVE = STAGE_BYTES / 4 / 1024;   // 1 KiB per wave instruction: 8
+constexpr int DMA_PER_WAVE = STAGE_BYTES / 4 / 1024;   // each wave fills a quarter
+static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
+static_assert(STAGES >= 2 && BYTES <= 160 * 1024, "LDS ring must fit in 160 KiB");
+static_assert((STAGES - 1) * DMA_PER_WAVE <= 63, "vmcnt range");
+// Row r's logical 16-byte chunk c is stored at physical chunk c ^ swz(r).
+// An LDS cycle serves 16 lanes of a ds_read_b128: rows r..r+15 (r a
+// multiple of 16) at one logical chunk. Rows repeat the 64-bank pattern
+// every 256 / ROWB rows, and swz spreads the 16 rows over 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
 }  // namespace dma
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -414,78 +433,167 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 #define MA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-// One k-tile: issue this wave's DMA of a later tile into `fill` (when
-// do_fill), then multiply the tile in `cur`. The two stage pointers are
-// distinct (__restrict__), which lets the compiler see that the fragment
-// reads of `cur` do not depend on the DMA into `fill`.
-//
-// e_blk >= 0 (AXPY only): this k-tile's 32 values of k are the rows
-// i_blk = e_blk of this wave's output block, and the Q fragments (X^T rows j)
-// hold X^T[j][i] = X[i][j] for them: the term a*X is added to the fp32
-// accumulators here instead of being read back from memory in the epilogue.
-__device__ __forceinline__ void dma_ktile(const unsigned char* __restrict__ cur, unsigned char* __restrict__ fill,
-                                          bool do_fill, const uint16_t* src, int ld_src, int lane_off,
-                                          int k0, int lane, int wm, int wn, f32x16_t (&acc)[4][4], int e_blk,
-                                          float a_coef) {
+// wait until at most `tiles` k-tile DMAs of this wave are outstanding
+__device__ __forceinline__ void dma_wait_tiles(int tiles) {
   using namespace dma;
-  if (do_fill) {
-    // this wave fills 8 KiB of the stage: rows [w*128, w*128+128) of P or Q
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q)
-      __builtin_amdgcn_global_load_lds(src + (int64_t)(q * 16) * ld_src + lane_off + k0,
-                                       (lds_void_t*)(fill + q * 1024), 16, 0, 0);
+  switch (tiles) {
+    case 0: MA_WAIT_VMCNT(0); break;
+    case 1: MA_WAIT_VMCNT(1 * DMA_PER_WAVE); break;
+    case 2: MA_WAIT_VMCNT((STAGES > 2 ? 2 : 1) * DMA_PER_WAVE); break;
+    case 3: MA_WAIT_VMCNT((STAGES > 3 ? 3 : 1) * DMA_PER_WAVE); break;
+    default: MA_WAIT_VMCNT((STAGES > 4 ? 4 : 1) * DMA_PER_WAVE); break;
   }
-  // fragments: row r, logical 16-byte chunk c stored at chunk c ^ ((r >> 2) & 3)
+}
+
+// Fragment reads of MFMA k-step kk (16 values of k) of a k-tile: this wave's
+// four 32-row blocks of P (fa) and of Q (fb); lane (l32, lh) reads row l32
+// of each block at logical chunk 2 kk + lh.
+__device__ __forceinline__ void dma_read_step(const unsigned char* cur, int kk, int lane, int wm, int wn,
+                                              u32x4_t (&fa)[4], u32x4_t (&fb)[4]) {
+  using namespace dma;
+  const int l32 = lane & 31, c = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + l32;
+    fa[i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = BM + wn * 128 + j * 32 + l32;
+    fb[j] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
+  }
+}
+
+// This wave's DMA of one k-tile (a quarter of the stage: rows
+// [w*128, w*128+128) of P or Q) into `fill`. Instruction q covers rows
+// q*RPI .. q*RPI+RPI-1 of the wave's panel; lane i lands at byte 1024 q + 16 i
+// (row q*RPI + i/CPR, physical chunk i%CPR) and so loads logical chunk
+// (i%CPR) ^ swz(row) from memory: lane_off[q & 1] holds that offset.
+__device__ __forceinline__ void dma_issue(unsigned char* fill, const uint16_t* src, int ld_src,
+                                          const int (&lane_off)[2], int k0) {
+  using namespace dma;
+#pragma unroll
+  for (int q = 0; q < DMA_PER_WAVE; ++q)
+    __builtin_amdgcn_global_load_lds(src + (int64_t)(q * RPI) * ld_src + lane_off[q & 1] + k0,
+                                     (lds_void_t*)(fill + q * 1024), 16, 0, 0);
+}
+
+// One DMA instruction q of this wave's share of a k-tile (see dma_issue)
+__device__ __forceinline__ void dma_issue_one(unsigned char* fill, const uint16_t* src, int ld_src,
+                                              const int (&lane_off)[2], int k0, int q) {
+  using namespace dma;
+  __builtin_amdgcn_global_load_lds(src + (int64_t)(q * RPI) * ld_src + lane_off[q & 1] + k0,
+                                   (lds_void_t*)(fill + q * 1024), 16, 0, 0);
+}
+
+// MFMAs of one k-step for accumulator rows [I0, I1)
+template <int I0, int I1>
+__device__ __forceinline__ void mfma_rows(f32x16_t (&acc)[4][4], const u32x4_t (&fa)[4], const u32x4_t (&fb)[4]) {
+#pragma unroll
+  for (int i = I0; i < I1; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mfma_frag<DT_BF16>(acc[i][j], fa[i], fb[j]);
+}
+
+// acc[II][j] += (a I) X^T-block for k-step h (0 or 1) of row block II, with
+// a = a_hi + a_lo (both exact in bf16). Lane (l32, lh) holds k = 16 h + 8 lh + e
+// of the block, and row i = l32 of a I is nonzero only at k = i.
+template <int II>
+__device__ __forceinline__ void ident_step(f32x16_t (&acc)[4][4], const u32x4_t (&fb)[4], int h, int lane,
+                                           float a_coef) {
   const int l32 = lane & 31, lh = lane >> 5;
-  u32x4_t fa[2][4], fb[2][4];
+  const float a_hi = __builtin_bit_cast(float, __float_as_uint(a_coef) & 0xFFFF0000u);
+  const float a_lo = a_coef - a_hi;
+  const uint32_t hi16 = __float_as_uint(a_hi) >> 16;
+  const uint32_t lo16 = pack_bf16x2(a_lo, 0.0f) & 0xFFFFu;
+  const int e = l32 - 16 * h - 8 * lh;   // the lane's nonzero slot, if in 0..7
+  u32x4_t id_hi = {0u, 0u, 0u, 0u}, id_lo = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int c = kk * 2 + lh;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + l32;
-      fa[kk][i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ ((r >> 2) & 3)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = BM + wn * 128 + j * 32 + l32;
-      fb[kk][j] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ ((r >> 2) & 3)) << 4));
-    }
+  for (int w = 0; w < 4; ++w) {
+    id_hi[w] = (e == 2 * w ? hi16 : 0u) | (e == 2 * w + 1 ? hi16 << 16 : 0u);
+    id_lo[w] = (e == 2 * w ? lo16 : 0u) | (e == 2 * w + 1 ? lo16 << 16 : 0u);
   }
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag<DT_BF16>(acc[i][j], fa[kk][i], fb[kk][j]);
-  if (e_blk >= 0) {
-    // acc[e_blk][j] += (a I) X^T-block: one more MFMA per fragment step with
-    // an identity A operand (a split as a_hi + a_lo, both exact in bf16) and
-    // the X^T fragment already in registers: lane (l32, lh) holds k =
-    // 16 kk + 8 lh + e, and row i = l32 of a I is nonzero only at k = i.
-    const float a_hi = __builtin_bit_cast(float, __float_as_uint(a_coef) & 0xFFFF0000u);
-    const float a_lo = a_coef - a_hi;
-    const uint32_t hi16 = __float_as_uint(a_hi) >> 16;
-    const uint32_t lo16 = pack_bf16x2(a_lo, 0.0f) & 0xFFFFu;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int e = l32 - 16 * kk - 8 * lh;   // the lane's nonzero slot, if in 0..7
-      u32x4_t id_hi = {0u, 0u, 0u, 0u}, id_lo = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        id_hi[w] = (e == 2 * w ? hi16 : 0u) | (e == 2 * w + 1 ? hi16 << 16 : 0u);
-        id_lo[w] = (e == 2 * w ? lo16 : 0u) | (e == 2 * w + 1 ? lo16 << 16 : 0u);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        if (ii != e_blk) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          mfma_frag<DT_BF16>(acc[ii][j], id_hi, fb[kk][j]);
-          mfma_frag<DT_BF16>(acc[ii][j], id_lo, fb[kk][j]);
-        }
-      }
+  for (int j = 0; j < 4; ++j) {
+    mfma_frag<DT_BF16>(acc[II][j], id_hi, fb[j]);
+    mfma_frag<DT_BF16>(acc[II][j], id_lo, fb[j]);
+  }
+}
+
+struct DmaCtx {
+  unsigned char* smem;
+  unsigned char* wave_fill;
+  const uint16_t* src;
+  int ld_src, lane, wm, wn, nk;
+  int lane_off[2];
+  float a;
+};
+
+// k-step KKI of k-tile kt: its MFMAs run on the fragments in (fa, fb) while
+// the next k-step's fragments are read into (na, nb). At the last k-step the
+// next read is of the next tile, after the barrier that also releases this
+// tile's stage to the DMA of tile kt + STAGES.
+// IIB >= 0 (AXPY): this k-tile's values of k are rows of this wave's output
+// blocks IIB + KKI/2, and the Q fragments (X^T rows j) hold X^T[j][i] = X[i][j]
+// for them, so (a I) X^T-block adds the term a*X to the accumulators instead
+// of reading X back in the epilogue.
+template <int KKI, int IIB>
+__device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt, f32x16_t (&acc)[4][4], u32x4_t (&fa)[4],
+                                          u32x4_t (&fb)[4], u32x4_t (&na)[4], u32x4_t (&nb)[4]) {
+  using namespace dma;
+  const int s_cur = kt % STAGES;
+  if constexpr (KKI + 1 < KK) {
+    // the first row block goes before the reads, so that the wait for (fa, fb)
+    // (read during the previous k-step) is not also a wait for the new reads
+    mfma_rows<0, 1>(acc, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_read_step(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows<1, 4>(acc, fa, fb);
+  } else {
+    // this wave's reads of tile kt are complete (on every path, so that the
+    // MFMAs below need no wait for them)
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (kt + 1 < c.nk) {
+      // tiles up to min(nk-1, kt+STAGES-1) have been issued: tile kt+1 has
+      // landed for this wave once only the later ones are outstanding; after
+      // the barrier every wave has read all of tile kt, so its stage may be
+      // refilled with tile kt+STAGES
+      const int later = c.nk - 2 - kt;
+      dma_wait_tiles(later < STAGES - 2 ? later : STAGES - 2);
+      __builtin_amdgcn_s_barrier();
+      dma_read_step(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // the DMA of tile kt+STAGES into the stage just released, one instruction
+    // between MFMAs: issued back to back, the four waves' instructions queue
+    // at the CU's one texture-address unit and hold up the MFMAs behind them
+    const bool fill = kt + STAGES < c.nk;
+    unsigned char* fill_at = c.wave_fill + s_cur * STAGE_BYTES;
+    const int k0 = (kt + STAGES) * BK;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_frag<DT_BF16>(acc[idx / 4][idx % 4], fa[idx / 4], fb[idx % 4]);
+#pragma unroll
+      for (int q = idx * DMA_PER_WAVE / 16; q < (idx + 1) * DMA_PER_WAVE / 16; ++q)
+        if (fill) dma_issue_one(fill_at, c.src, c.ld_src, c.lane_off, k0, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if constexpr (IIB >= 0) ident_step<IIB + KKI / 2>(acc, fb, KKI % 2, c.lane, c.a);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One k-tile: KK k-steps, the fragment sets alternating (0, 1) -> (1, 0) -> ...
+// so that (f0a, f0b) again hold the next tile's first k-step afterwards.
+template <int IIB>
+__device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt, f32x16_t (&acc)[4][4], u32x4_t (&f0a)[4],
+                                          u32x4_t (&f0b)[4], u32x4_t (&f1a)[4], u32x4_t (&f1b)[4]) {
+  dma_kstep<0, IIB>(c, kt, acc, f0a, f0b, f1a, f1b);
+  dma_kstep<1, IIB>(c, kt, acc, f1a, f1b, f0a, f0b);
+  if constexpr (dma::KK == 4) {
+    dma_kstep<2, IIB>(c, kt, acc, f0a, f0b, f1a, f1b);
+    dma_kstep<3, IIB>(c, kt, acc, f1a, f1b, f0a, f0b);
   }
 }
 
@@ -497,23 +605,28 @@ ns_gemm_dma(const NsArgs args) {
   TileJob J;
   if (!map_job(args, J)) return;
   const NsGroup& G = args.g[J.gi];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // DMA source of this wave: waves 0,1 load P rows [w*128, +128), waves 2,3
-  // Q rows [(w-2)*128, +128). Lane i of instruction q lands in the stage at
-  // byte (w*8 + q)*1024 + 16 i, i.e. tile row (w*8+q)*16 + i/4 (P and Q rows
-  // are contiguous), physical chunk i%4 holding logical chunk
-  // (i%4) ^ ((row >> 2) & 3) = (i%4) ^ ((i/16) & 3). With 64-byte rows, the
-  // 16 lanes an LDS cycle serves (rows r..r+15 of one chunk column) then hit
-  // 16 distinct 16-byte bank groups.
+  // Q rows [(w-2)*128, +128); P and Q rows are contiguous in the stage.
+  DmaCtx c;
+  c.smem = smem;
+  c.wave_fill = smem + wave * (DMA_PER_WAVE * 1024);
+  c.lane = lane;
+  c.wm = wave >> 1;
+  c.wn = wave & 1;
+  c.nk = G.K / BK;   // K is a multiple of 256: nk >= 4
+  c.a = args.a;
   const bool isP = wave < 2;
-  const int ld_src = isP ? G.ldP : G.ldQ;
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) +
-                        (int64_t)J.mat * (isP ? G.sP : G.sQ) +
-                        (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave & 1) * 128) * ld_src;
-  const int lane_off = (lane >> 2) * ld_src + (((lane & 3) ^ ((lane >> 4) & 3)) << 3);
-  unsigned char* wave_fill = smem + wave * (DMA_PER_WAVE * 1024);
+  c.ld_src = isP ? G.ldP : G.ldQ;
+  c.src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
+          (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave & 1) * 128) * c.ld_src;
+  // instruction q adds q*RPI rows; swz of the stage row depends on q only
+  // through q & 1 (panels start at multiples of 128 rows)
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    c.lane_off[par] = (lane / CPR) * c.ld_src + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -523,30 +636,34 @@ ns_gemm_dma(const NsArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = G.K / BK;   // K is a multiple of 256: nk >= 8
-  // prologue: tiles 0 and 1 into stages 0 and 1
+  // Pipeline over k-tiles kt (stage kt % S, S = STAGES): the DMA of tile
+  // kt+S is issued during tile kt, once every wave has read all of tile kt,
+  // and each k-step's fragments are read while the previous k-step's MFMAs
+  // run.
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q)
-      __builtin_amdgcn_global_load_lds(src + (int64_t)(q * 16) * ld_src + lane_off + t * BK,
-                                       (lds_void_t*)(wave_fill + t * STAGE_BYTES + q * 1024), 16, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt has landed for this wave once at most the DMA of tile kt+1 is
-    // outstanding; the barrier makes that true for every wave, and also
-    // guarantees every wave is done reading the stage the next DMA refills
-    if (kt + 1 < nk) MA_WAIT_VMCNT(dma::DMA_PER_WAVE);
-    else MA_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
-    const int s_cur = kt % STAGES, s_fill = (kt + 2) % STAGES;
-    int e_blk = -1;
-    if constexpr (EPI == EPI_AXPY) {
-      const int d = kt * BK - (J.bi * BM + wm * 128);
-      if (d >= 0 && d < 128) e_blk = d >> 5;
+  for (int t = 0; t < STAGES; ++t)
+    dma_issue(c.wave_fill + t * STAGE_BYTES, c.src, c.ld_src, c.lane_off, t * BK);
+  dma_wait_tiles(STAGES - 1);   // this wave's part of tile 0 has landed
+  __builtin_amdgcn_s_barrier();
+  u32x4_t f0a[4], f0b[4], f1a[4], f1b[4];
+  dma_read_step(smem, 0, lane, c.wm, c.wn, f0a, f0b);
+  int kt = 0;
+  if constexpr (EPI == EPI_AXPY) {
+    // the k-tiles whose k range is this wave's 128 output rows (K = m_pad,
+    // so they lie inside [0, nk)) carry the a*X term
+    const int e_first = (J.bi * BM + c.wm * 128) / BK;
+    for (; kt < e_first; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
+    if constexpr (BK == 32) {
+      dma_ktile<0>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<1>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<2>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<3>(c, kt++, acc, f0a, f0b, f1a, f1b);
+    } else {
+      dma_ktile<0>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<2>(c, kt++, acc, f0a, f0b, f1a, f1b);
     }
-    dma_ktile(smem + s_cur * STAGE_BYTES, wave_fill + s_fill * STAGE_BYTES, kt + 2 < nk, src, ld_src, lane_off,
-              (kt + 2) * BK, lane, wm, wn, acc, e_blk, args.a);
   }
+  for (; kt < c.nk; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
   ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, EPI == EPI_AXPY>(args, G, J, acc, smem);
 }
@@ -580,6 +697,8 @@ static hipError_t launch_dma(const NsArgs& a, hipStream_t s) {
 #define MA_NS_TILE(BM_, BN_, BK_, WGM_, WGN_)                                                      \
   if (tile.bm == BM_ && tile.bn == BN_ && tile.bk == BK_ && tile.wgm == WGM_ && tile.wgn == WGN_) \
     return launch_reg_epi<DTv, BM_, BN_, BK_, WGM_, WGN_>(epi, a, s);
+
+int ns_dma_bk() { return dma::BK; }
 
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipStream_t s) {
   if (a.padded_blocks <= 0) return hipSuccess;

@@ -54,4 +54,7 @@ struct NsTile { int bm, bn, bk, wgm, wgn, dma; };
 
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& args, hipStream_t s);
 
+// k-tile of the LDS-DMA kernel (its block tile is 256 x 256, 2 x 2 waves)
+int ns_dma_bk();
+
 }  // namespace ma
