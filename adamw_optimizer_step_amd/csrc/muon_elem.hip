@@ -56,15 +56,27 @@ __global__ void __launch_bounds__(256) k_rowsumsq_momentum(const ElemArgs a) {
     const int64_t base = (int64_t)r * a.C;
     float acc = 0.0f;
     if (a.vec) {
-      for (int c = lane * 8; c < a.C; c += 512) {
-        float g[8], m[8];
-        load8<DTG>(eptr<DTG>(gp, base + c), g);
-        load8<DTM>(eptr<DTM>(mp, base + c), m);
+      // up to 4 chunks of 8 per lane in flight before any arithmetic
+      for (int c0 = lane * 8; c0 < a.C; c0 += 4 * 512) {
+        float g[4][8], m[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float m1, mt;
-          momentum1(g[e], m[e], a.beta, a.nesterov, m1, mt);
-          acc = __builtin_fmaf(mt, mt, acc);
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 512;
+          if (c < a.C) {
+            load8<DTG>(eptr<DTG>(gp, base + c), g[u]);
+            load8<DTM>(eptr<DTM>(mp, base + c), m[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (c0 + u * 512 < a.C) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float m1, mt;
+              momentum1(g[u][e], m[u][e], a.beta, a.nesterov, m1, mt);
+              acc = __builtin_fmaf(mt, mt, acc);
+            }
+          }
         }
       }
     } else {
@@ -230,6 +242,53 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
   }
 }
 
+__device__ __forceinline__ float post_elem(float w, float u, float f, bool has_f, const ElemArgs& a) {
+  const float ue = has_f ? __fmul_rn(u, f) : u;
+  const bool mask = a.cautious ? (__fmul_rn(ue, w) >= 0.0f) : true;
+  const float w1 = (a.decay && mask) ? __fsub_rn(w, __fmul_rn(a.c_wd, w)) : w;
+  return __fsub_rn(w1, __fmul_rn(a.c_lr, ue));
+}
+
+constexpr int kPostChunks = 4;   // 8-element chunks per thread (vector path)
+
+// Vector path (C % 8 == 0, 16-byte aligned rows): the matrices' 8-element
+// chunks in row-major order; thread t of block b takes chunks
+// (b*256 + t) + 256*blocks*u... of its matrix, all loads before any update.
+template <int DTP, int DTX>
+__global__ void __launch_bounds__(256) k_post_vec(const ElemArgs a, int blocks_per_mat) {
+  const int k = blockIdx.x / blocks_per_mat;
+  const int b = blockIdx.x - k * blocks_per_mat;
+  const uint32_t cpr = (uint32_t)a.C >> 3;                 // chunks per row
+  const uint32_t nch = (uint32_t)a.R * cpr;                // < 2^28: a matrix holds < 2^31 elements
+  void* wp = a.mat[k].w;
+  const void* xd = eptr<DTX>(static_cast<const void*>(a.xd), (int64_t)k * a.x_stride);
+  const float* rowf = a.rowf ? a.rowf + (int64_t)k * a.row_stride : nullptr;
+  const uint32_t step = (uint32_t)blocks_per_mat * 256u;
+  for (uint32_t q0 = (uint32_t)b * 256u + threadIdx.x; q0 < nch; q0 += step * kPostChunks) {
+    float w[kPostChunks][8], u[kPostChunks][8];
+    uint32_t rr[kPostChunks], cc[kPostChunks];
+#pragma unroll
+    for (int v = 0; v < kPostChunks; ++v) {
+      const uint32_t q = q0 + step * v;
+      rr[v] = q / cpr;
+      cc[v] = (q - rr[v] * cpr) * 8u;
+      if (q < nch) {
+        load8<DTP>(eptr<DTP>(static_cast<const void*>(wp), (int64_t)rr[v] * a.C + cc[v]), w[v]);
+        load8<DTX>(eptr<DTX>(xd, (int64_t)rr[v] * a.ld_d + cc[v]), u[v]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < kPostChunks; ++v) {
+      if (q0 + step * v < nch) {
+        const float f = rowf ? rowf[rr[v]] : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[v][e] = post_elem(w[v][e], u[v][e], f, rowf != nullptr, a);
+        store8<DTP>(eptr<DTP>(wp, (int64_t)rr[v] * a.C + cc[v]), w[v]);
+      }
+    }
+  }
+}
+
 // W <- RNE( (mask ? W - c_wd*W : W) - c_lr*U ), mask = cautious ? (U*W >= 0) : 1.
 template <int DTP, int DTX>
 __global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
@@ -243,7 +302,6 @@ __global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
   const int tid = threadIdx.x;
   const int cl = (tid & 7) * 8;
   const bool vec = a.vec && (a.ld_d & 7) == 0;
-  const float clr = a.c_lr, cwd = a.c_wd;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = r0 + (tid >> 3) + 32 * h, c = c0 + cl;
@@ -264,12 +322,7 @@ __global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ue = a.rowf ? __fmul_rn(u[e], f) : u[e];
-      const bool mask = a.cautious ? (__fmul_rn(ue, w[e]) >= 0.0f) : true;
-      const float w1 = (a.decay && mask) ? __fsub_rn(w[e], __fmul_rn(cwd, w[e])) : w[e];
-      w[e] = __fsub_rn(w1, __fmul_rn(clr, ue));
-    }
+    for (int e = 0; e < 8; ++e) w[e] = post_elem(w[e], u[e], f, a.rowf != nullptr, a);
     if (vec) {
       store8<DTP>(eptr<DTP>(wp, off), w);
     } else {
@@ -334,6 +387,16 @@ hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream
 }
 
 hipError_t launch_post(int dt_p, int dt_x, const ElemArgs& a, hipStream_t s) {
+  if (a.count <= 0 || a.R <= 0 || a.C <= 0) return hipSuccess;
+  if (a.vec && (a.C & 7) == 0 && (a.ld_d & 7) == 0) {
+    // about 4 chunks per thread: enough blocks to fill the chip without tiny blocks
+    const int64_t nch = (int64_t)a.R * (a.C >> 3);
+    int64_t bpm = (nch + 256 * kPostChunks - 1) / (256 * kPostChunks);
+    if (bpm < 1) bpm = 1;
+    const int bpm_i = (int)bpm;
+    MA_DISPATCH2(dt_p, dt_x, k_post_vec, dim3(a.count * bpm_i), dim3(256), 0, s, a, bpm_i);
+    return hipGetLastError();
+  }
   const int blocks = a.count * a.tiles_r * a.tiles_c;
   if (blocks <= 0) return hipSuccess;
   MA_DISPATCH2(dt_p, dt_x, k_post, dim3(blocks), dim3(256), 0, s, a);
