@@ -263,6 +263,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
     if (plan.g[i].count > 0) order.push_back(i);
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return plan.g[a].n_pad > plan.g[b].n_pad; });
   const int64_t e = dt_bytes(dtype);
+
   for (int step = 0; step < T; ++step) {
     const int cur = step & 1, nxt = cur ^ 1;
     const bool last = step == T - 1;
@@ -339,6 +340,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
         }
         A.per_xcd = per_xcd;
         A.padded_blocks = 8 * per_xcd;
+        if (tile.dma) A.padded_blocks = 8 * std::min(per_xcd, kNsPersBlocksPerXcd);
         hipError_t err;
         {
           ProfScope ps(MA_K_GRAM + epi, s);
@@ -683,6 +685,7 @@ int ma_test_ns(int64_t m, int64_t n, int32_t count, int32_t precision, const voi
   GroupPlan& p = plan.g[0];
   size_t off = 0;
   plan_group(p, m, n, count, precision, off);
+  plan.bytes = off;
   p.dt_p = p.dt_g = p.dt_m = precision;
   p.src = nullptr;
   if (!workspace || workspace_bytes < off || (uintptr_t)workspace % MA_WORKSPACE_ALIGN)

@@ -67,12 +67,12 @@ struct TileJob {
   int gi, mat, bi, bj;
 };
 
-__device__ __forceinline__ bool map_job(const NsArgs& args, TileJob& J) {
-  const int x = (int)(blockIdx.x & 7);
-  int local = (int)(blockIdx.x >> 3);
+// Job `local` of XCD x's list (see NsArgs); false past its end.
+__device__ __forceinline__ bool map_job_at(const NsArgs& args, int x, int local, TileJob& J) {
   // walk the groups in order; XCD x owns units u0, u0+8, ... of each, where
-  // u0 = (x - rot) mod 8
-#pragma unroll
+  // u0 = (x - rot) mod 8. Not unrolled: a persistent caller would otherwise
+  // keep every group's fields live in scalar registers across its job loop.
+#pragma unroll 1
   for (int q = 0; q < kMaxNsGroups; ++q) {
     if (q >= args.n_groups) return false;
     const NsGroup& G = args.g[q];
@@ -106,6 +106,10 @@ __device__ __forceinline__ bool map_job(const NsArgs& args, TileJob& J) {
   return false;
 }
 
+__device__ __forceinline__ bool map_job(const NsArgs& args, TileJob& J) {
+  return map_job_at(args, (int)(blockIdx.x & 7), (int)(blockIdx.x >> 3), J);
+}
+
 // ---------------------------------------------------------------------------
 // epilogue: a/b/c combination, then staged, coalesced stores
 // ---------------------------------------------------------------------------
@@ -123,7 +127,7 @@ struct EpiSmem {
 template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false>
 __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
-                                            unsigned char* smem) {
+                                            unsigned char* smem, int tid_in = -1) {
   using Tr = MfmaTraits<DT>;
   using T = typename Tr::T;
   using ES = EpiSmem<DT, BM, BN>;
@@ -131,7 +135,7 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int VEC = 16 / Tr::kElem;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tid_in >= 0 ? tid_in : (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, lh = lane >> 5;
   const int mat = J.mat, bi = J.bi, bj = J.bj;
@@ -597,16 +601,19 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt, f32x16_t (&ac
   }
 }
 
+// One output tile: prologue DMA, main loop, epilogue.
 template <int EPI>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-ns_gemm_dma(const NsArgs args) {
+__device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem) {
   using namespace dma;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES];
-  TileJob J;
-  if (!map_job(args, J)) return;
   const NsGroup& G = args.g[J.gi];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // an opaque copy of the thread index: without it the compiler hoists every
+  // lane-dependent address of the tile out of a persistent block's job loop
+  // and keeps them all live, through the epilogue too
+  int opaque;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(opaque) : "v"((int)threadIdx.x));
+  const int lane = opaque & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int tid = (wave << 6) | lane;
 
   // DMA source of this wave: waves 0,1 load P rows [w*128, +128), waves 2,3
   // Q rows [(w-2)*128, +128); P and Q rows are contiguous in the stage.
@@ -665,7 +672,27 @@ ns_gemm_dma(const NsArgs args) {
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, EPI == EPI_AXPY>(args, G, J, acc, smem);
+  ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, EPI == EPI_AXPY>(args, G, J, acc, smem, tid);
+}
+
+// Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
+// runs jobs b/8, b/8 + P, b/8 + 2P, ... of that list. With at most one block
+// per CU this saves a block launch and its set-up per tile; the lists hold
+// the longest jobs first and, where jobs differ in K, a fixed stride ends
+// about as late as taking jobs on demand would (the blocks holding one long
+// and two short jobs set the end either way).
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ns_gemm_dma(const NsArgs args) {
+  using namespace dma;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES];
+  const int x = (int)(blockIdx.x & 7);
+  const int P = (int)(gridDim.x >> 3);
+  TileJob J;
+  for (int local = (int)(blockIdx.x >> 3); map_job_at(args, x, local, J); local += P) {
+    dma_tile<EPI>(args, J, smem);
+    __syncthreads();   // the epilogue is done with LDS before the next job's DMA
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -40,13 +40,18 @@ struct NsGroup {
 // gets one eighth of every group (balanced when groups differ in K) and, for
 // whole-matrix units, all tiles of a matrix share one L2. Each group's first
 // unit goes to the XCD after the previous group's last one.
+//
+// The LDS-DMA kernel is persistent: padded_blocks = 8 x P with P <= 32 (one
+// block per CU); block b runs jobs b/8, b/8 + P, ... of XCD b % 8.
 struct NsArgs {
   int32_t n_groups;
-  int32_t per_xcd;         // blocks per XCD (max over XCDs of their job count)
-  int32_t padded_blocks;   // 8 * per_xcd
+  int32_t per_xcd;         // jobs of the busiest XCD
+  int32_t padded_blocks;   // blocks launched
   float a, b, c;
   NsGroup g[kMaxNsGroups];
 };
+
+constexpr int kNsPersBlocksPerXcd = 32;   // CUs per XCD
 
 // tile configuration chosen per launch: block tile bm x bn, K tile bk,
 // wgm x wgn waves; dma selects the LDS-DMA kernel (bf16, 256 x 256 x 32)
