@@ -9,8 +9,14 @@ from .api import (  # noqa: F401
     muon_step, muon_workspace_size, muon_workspace_update, newton_schulz, update_stage,
 )
 from ._lib import MuonAdamWError, lib  # noqa: F401
+from .coefficients import keller_jordan, polar_express  # noqa: F401
+
+# Polar Express table for 5 steps: greedy per-step minimax from singular
+# values in [1e-3, 1], each polynomial evaluated at x / 1.01 (headroom for
+# bf16 rounding at the top of the spectrum); see ``coefficients``.
+POLAR_EXPRESS = tuple(polar_express(5, lower=1e-3, safety=1.01))
 
 __all__ = [
-    "KELLER_JORDAN", "MuonGroup", "MuonHParams", "MuonAdamWError", "adamw_step", "muon_step",
+    "KELLER_JORDAN", "POLAR_EXPRESS", "keller_jordan", "polar_express", "MuonGroup", "MuonHParams", "MuonAdamWError", "adamw_step", "muon_step",
     "muon_workspace_size", "muon_workspace_update", "lib",
 ]

@@ -19,8 +19,8 @@ MA_ERR_HIP = -4
 
 MA_F32 = 0
 MA_BF16 = 1
-MA_EQ_OFF, MA_EQ_ROWS_PRE, MA_EQ_ROWS_POST = 0, 1, 2
-MA_SCALE_NONE, MA_SCALE_SQRT_MAX1_R_OVER_C = 0, 1
+MA_EQ_OFF, MA_EQ_ROWS_PRE, MA_EQ_ROWS_POST, MA_EQ_ROWS_RMS = 0, 1, 2, 3
+MA_SCALE_NONE, MA_SCALE_SQRT_MAX1_R_OVER_C, MA_SCALE_MOONSHOT, MA_SCALE_SQRT_MAX = 0, 1, 2, 3
 MA_MAX_NS_STEPS = 16
 KERNEL_KINDS = ("rownorm", "finalize", "pre", "gram", "poly", "axpy", "post", "adamw")
 MA_WORKSPACE_ALIGN = 256

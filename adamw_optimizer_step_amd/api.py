@@ -20,8 +20,9 @@ KELLER_JORDAN = (3.4445, -4.7750, 2.0315)
 
 _DT = {torch.bfloat16: L.MA_BF16, torch.float32: L.MA_F32}
 _PREC = {"bf16": L.MA_BF16, "f32": L.MA_F32}
-_EQ = {"off": L.MA_EQ_OFF, "pre": L.MA_EQ_ROWS_PRE, "post": L.MA_EQ_ROWS_POST}
-_SCALE = {"none": L.MA_SCALE_NONE, "sqrt_max1_r_over_c": L.MA_SCALE_SQRT_MAX1_R_OVER_C}
+_EQ = {"off": L.MA_EQ_OFF, "pre": L.MA_EQ_ROWS_PRE, "post": L.MA_EQ_ROWS_POST, "rms": L.MA_EQ_ROWS_RMS}
+_SCALE = {"none": L.MA_SCALE_NONE, "sqrt_max1_r_over_c": L.MA_SCALE_SQRT_MAX1_R_OVER_C,
+          "moonshot": L.MA_SCALE_MOONSHOT, "sqrt_max": L.MA_SCALE_SQRT_MAX}
 
 
 def _dt(t: torch.Tensor) -> int:

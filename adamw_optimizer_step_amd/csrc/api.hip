@@ -138,9 +138,9 @@ int validate_hparams(const ma_muon_hparams* hp) {
   if (hp->ns_steps < 0 || hp->ns_steps > MA_MAX_NS_STEPS)
     return fail(MA_ERR_INVALID_ARG, "ns_steps %d outside 0..%d", hp->ns_steps, MA_MAX_NS_STEPS);
   if (hp->ns_steps > 0 && !hp->abc) return fail(MA_ERR_INVALID_ARG, "abc is null with ns_steps > 0");
-  if (hp->equilibrate < MA_EQ_OFF || hp->equilibrate > MA_EQ_ROWS_POST)
+  if (hp->equilibrate < MA_EQ_OFF || hp->equilibrate > MA_EQ_ROWS_RMS)
     return fail(MA_ERR_INVALID_ARG, "equilibrate %d is not an ma_eq value", hp->equilibrate);
-  if (hp->lr_scale != MA_SCALE_NONE && hp->lr_scale != MA_SCALE_SQRT_MAX1_R_OVER_C)
+  if (hp->lr_scale < MA_SCALE_NONE || hp->lr_scale > MA_SCALE_SQRT_MAX)
     return fail(MA_ERR_INVALID_ARG, "lr_scale %d is not an ma_scale value", hp->lr_scale);
   if (!dt_valid(hp->ns_precision)) return fail(MA_ERR_UNSUPPORTED, "ns_precision %d", hp->ns_precision);
   if (!std::isfinite(hp->lr) || !std::isfinite(hp->momentum) || !std::isfinite(hp->weight_decay) ||
@@ -184,6 +184,16 @@ int validate_group(const ma_muon_group& g, int idx, bool need_ptrs) {
   return MA_OK;
 }
 
+// Per-matrix lr multiplier (see ma_scale), in double on the host.
+double lr_multiplier(int scale, int64_t R, int64_t C) {
+  switch (scale) {
+    case MA_SCALE_SQRT_MAX1_R_OVER_C: return std::sqrt(std::max(1.0, (double)R / (double)C));
+    case MA_SCALE_MOONSHOT: return 0.2 * std::sqrt((double)std::max(R, C));
+    case MA_SCALE_SQRT_MAX: return std::sqrt((double)std::max(R, C));
+    default: return 1.0;
+  }
+}
+
 int build_plan(const ma_muon_group* groups, int32_t n, const ma_muon_hparams* hp, Plan& plan,
                bool need_ptrs) {
   if (n < 0 || (n > 0 && !groups)) return fail(MA_ERR_INVALID_ARG, "groups is null or n_groups < 0");
@@ -199,8 +209,7 @@ int build_plan(const ma_muon_group* groups, int32_t n, const ma_muon_hparams* hp
     p.dt_p = groups[i].param_dtype;
     p.dt_g = groups[i].grad_dtype;
     p.dt_m = groups[i].mom_dtype;
-    const double mult = hp->lr_scale == MA_SCALE_SQRT_MAX1_R_OVER_C
-                            ? std::sqrt(std::max(1.0, (double)p.R / (double)p.C)) : 1.0;
+    const double mult = lr_multiplier(hp->lr_scale, p.R, p.C);
     const double lr_eff = (double)hp->lr * mult;
     p.c_lr = (float)lr_eff;
     p.c_wd = (float)(lr_eff * (double)hp->weight_decay);
@@ -474,8 +483,8 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
       ElemArgs a = elem_args(p, hp, ws, first, cnt);
       a.xd = ws + p.off_direct(ub) + (size_t)(first * p.x_stride * dt_bytes(p.dt_x));
       a.xt = nullptr;
-      if (hp->equilibrate == MA_EQ_ROWS_POST) {
-        a.finalize_mode = 2;
+      if (hp->equilibrate == MA_EQ_ROWS_POST || hp->equilibrate == MA_EQ_ROWS_RMS) {
+        a.finalize_mode = hp->equilibrate == MA_EQ_ROWS_POST ? 2 : 3;
         { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_buffer(p.dt_x, a, s); }
         if (err != hipSuccess) return hip_fail(err, "update row norms");
         { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }

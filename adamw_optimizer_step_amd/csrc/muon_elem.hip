@@ -3,7 +3,8 @@
 //   k_rowsumsq_momentum  per row of the Nesterov look-ahead Mt = G + beta*m1,
 //                        m1 = beta*M + G: sum of squares (one wave per row,
 //                        16-byte loads, butterfly shuffle reduction; no atomics)
-//   k_finalize           per matrix: Frobenius scale, MuonEq row factors
+//   k_finalize           per matrix: Frobenius scale, MuonEq row factors,
+//                        NorMuon row factors
 //   k_pre                momentum update M <- m1 (stored), X0 = Mt * f_row,
 //                        written in the parameter's layout and transposed
 //                        (through an LDS tile) into the Newton-Schulz buffers
@@ -150,9 +151,13 @@ __global__ void __launch_bounds__(256) k_finalize(const ElemArgs a) {
   } else if (mode == 1) {
     const float s = 1.0f / (sqrtf(total) + a.norm_eps);
     for (int i = t; i < a.R; i += 256) rf[i] = s / (sqrtf(rs[i]) + a.eq_eps);
-  } else {
+  } else if (mode == 2) {
     const float rho = sqrtf(total) / sqrtf((float)a.R);
     for (int i = t; i < a.R; i += 256) rf[i] = rho / (sqrtf(rs[i]) + a.eq_eps);
+  } else {
+    // row RMS: ||U_i|| / sqrt(cols)
+    const float sc = sqrtf((float)a.C);
+    for (int i = t; i < a.R; i += 256) rf[i] = 1.0f / (sqrtf(rs[i]) / sc + a.eq_eps);
   }
 }
 

@@ -53,16 +53,32 @@ extern "C" {
 
 typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
 
-/* MuonEq row equilibration. PRE divides each row (output feature, in the
- * parameter's own layout) of the Nesterov look-ahead by its Euclidean norm
- * (+eq_eps) before the Frobenius normalisation; POST rescales each row of
- * the orthogonalised update to the matrix's mean row norm, ||U||_F/sqrt(rows),
- * over (||U_i|| + eq_eps). */
-typedef enum { MA_EQ_OFF = 0, MA_EQ_ROWS_PRE = 1, MA_EQ_ROWS_POST = 2 } ma_eq;
+/* Row scalings (rows are output features, in the parameter's own layout).
+ * ROWS_PRE (MuonEq): each row of the Nesterov look-ahead is divided by its
+ *   Euclidean norm (+eq_eps) before the Frobenius normalisation.
+ * ROWS_POST (MuonEq after the iteration): each row of the orthogonalised
+ *   update U is rescaled to the matrix's mean row norm, ||U||_F/sqrt(rows),
+ *   over (||U_i|| + eq_eps).
+ * ROWS_RMS (NorMuon, "Chapter 4: The MuonAdamW Optimizer", section "NorMuon:
+ *   Normalized Muon"): each row of U is divided by its RMS,
+ *   ||U_i||/sqrt(cols), plus eq_eps (the page uses 1e-8), so that with
+ *   lr_scale NONE every row of the step has RMS lr. */
+typedef enum { MA_EQ_OFF = 0, MA_EQ_ROWS_PRE = 1, MA_EQ_ROWS_POST = 2, MA_EQ_ROWS_RMS = 3 } ma_eq;
 
-/* Per-matrix lr multiplier: NONE = 1, SQRT_MAX1_R_OVER_C = sqrt(max(1, rows/cols))
- * (nanochat discussion, reply by mira687: x2 for c_fc, x1 for c_proj). */
-typedef enum { MA_SCALE_NONE = 0, MA_SCALE_SQRT_MAX1_R_OVER_C = 1 } ma_scale;
+/* Per-matrix lr multiplier:
+ *   NONE                1
+ *   SQRT_MAX1_R_OVER_C  sqrt(max(1, rows/cols)) (nanochat discussion, reply by
+ *                       mira687: x2 for c_fc, x1 for c_proj)
+ *   MOONSHOT            0.2 * sqrt(max(rows, cols)) ("Muon vs AdamW, Lion and
+ *                       Sophia: a fair race": entries about AdamW's size)
+ *   SQRT_MAX            sqrt(max(rows, cols)) ("3.9 Optimizers ...", section
+ *                       "Muon: Orthogonalizing the Update": update RMS about 1) */
+typedef enum {
+  MA_SCALE_NONE = 0,
+  MA_SCALE_SQRT_MAX1_R_OVER_C = 1,
+  MA_SCALE_MOONSHOT = 2,
+  MA_SCALE_SQRT_MAX = 3
+} ma_scale;
 
 /* One group: `count` matrices of identical shape rows x cols.
  * params/grads/momentum are HOST arrays of `count` DEVICE pointers; matrix i
@@ -93,7 +109,8 @@ typedef struct {
  *                 MA_F32: iterate in fp32
  *   lr_scale      ma_scale
  *   norm_eps      added to the Frobenius norm (the pages use 1e-7)
- *   eq_eps        added to each row norm by MuonEq (1e-7) */
+ *   eq_eps        added to each row norm by MuonEq (1e-7), or to each row RMS
+ *                 by ROWS_RMS */
 typedef struct {
   float lr, momentum, weight_decay;
   int32_t nesterov, ns_steps;
@@ -134,8 +151,8 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
 
 /* Where matrix `index` of group `group` keeps the result of its Newton-Schulz
  * iteration inside a workspace after ma_muon_step (for inspection; valid
- * until the workspace is reused; with MA_EQ_ROWS_POST the row scaling is
- * applied later, in the update, and is not included). *u receives a DEVICE
+ * until the workspace is reused; with MA_EQ_ROWS_POST or MA_EQ_ROWS_RMS the
+ * row scaling is applied later, in the update, and is not included). *u receives a DEVICE
  * pointer into `workspace`, in the parameter's layout (rows x cols, row pitch
  * *ld elements); *transposed (may be null) is set to 0; *elem_bytes is 2
  * (bf16 iteration) or 4 (fp32). */

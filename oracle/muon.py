@@ -78,9 +78,26 @@ def coefficient_schedule(coeffs, ns_steps=None) -> Tuple[Tuple[float, float, flo
     return steps
 
 
-def lr_multiplier(rows: int, cols: int) -> float:
-    """``sqrt(max(1, rows/cols))`` (nanochat discussion, reply by mira687)."""
-    return math.sqrt(max(1.0, rows / cols))
+def lr_multiplier(rows: int, cols: int, scale="sqrt_max1_r_over_c") -> float:
+    """Per-matrix lr multiplier.
+
+    * ``"sqrt_max1_r_over_c"`` (or True): ``sqrt(max(1, rows/cols))`` (nanochat
+      discussion, reply by mira687);
+    * ``"moonshot"``: ``0.2 * sqrt(max(rows, cols))`` ("Muon vs AdamW, Lion and
+      Sophia: a fair race", the Muon section);
+    * ``"sqrt_max"``: ``sqrt(max(rows, cols))`` ("3.9 Optimizers ...", section
+      "Muon: Orthogonalizing the Update");
+    * ``"none"`` (or False): 1.
+    """
+    if scale is True or scale == "sqrt_max1_r_over_c":
+        return math.sqrt(max(1.0, rows / cols))
+    if scale == "moonshot":
+        return 0.2 * math.sqrt(max(rows, cols))
+    if scale == "sqrt_max":
+        return math.sqrt(max(rows, cols))
+    if scale is False or scale == "none":
+        return 1.0
+    raise ValueError(f"unknown lr scale {scale!r}")
 
 
 def momentum_stage(g, m, beta: float, nesterov: bool = True):
@@ -198,14 +215,14 @@ def muon_step(W, G, M, *, lr: float, momentum: float = 0.95, nesterov: bool = Tr
               coeffs=KELLER_JORDAN, ns_steps: int | None = 5, weight_decay: float = 0.0,
               cautious: bool = False, equilibrate: str = "off", precision: str = "bf16",
               param_dtype: str = "bf16", mom_dtype: str = "bf16", norm_eps: float = 1e-7,
-              eq_eps: float = 1e-7, lr_scale: bool = True):
+              eq_eps: float = 1e-7, lr_scale="sqrt_max1_r_over_c"):
     """One Muon step for one ``rows x cols`` matrix.
 
     Inputs are arrays holding the stored values (bf16 values as float32).
     Returns a dict with the stored new weight ``W`` and buffer ``M``, the
     update direction ``U`` the decay and update consumed (binary32, param
-    layout), ``U_ns`` the Newton-Schulz result before any MuonEq POST row
-    scaling, ``X0`` (float64), the mask and the binary32 scalars used.
+    layout), ``U_ns`` the Newton-Schulz result before any row scaling after
+    the iteration (MuonEq POST, NorMuon), ``X0`` (float64), the mask and the binary32 scalars used.
     """
     W = np.asarray(W, dtype=f32)
     R, C = W.shape
@@ -219,8 +236,14 @@ def muon_step(W, G, M, *, lr: float, momentum: float = 0.95, nesterov: bool = Tr
         rho = math.sqrt(float(np.sum(Uf * Uf))) / math.sqrt(R)
         rn = np.sqrt(row_sumsq(Uf))
         U = Uf * (rho / (rn + eq_eps))[:, None]
+    elif equilibrate == "rms":
+        # NorMuon ("Chapter 4", section "NorMuon: Normalized Muon"): each row
+        # divided by its RMS, ||U_i|| / sqrt(cols), plus eq_eps
+        Uf = np.asarray(U, dtype=f64)
+        rms = np.sqrt(row_sumsq(Uf)) / math.sqrt(C)
+        U = Uf / (rms + eq_eps)[:, None]
     u = np.asarray(U, dtype=f32)
-    lr_eff = lr * (lr_multiplier(R, C) if lr_scale else 1.0)
+    lr_eff = lr * lr_multiplier(R, C, lr_scale)
     c_lr, c_wd = f32(lr_eff), f32(lr_eff * weight_decay)
     w2, mask = post_stage(W, u, c_lr, c_wd, cautious, decay=(weight_decay != 0.0))
     return {"W": _store(w2, param_dtype), "M": M_new, "U": u, "U_ns": U_ns, "X0": x0, "mask": mask,

@@ -85,6 +85,28 @@ def test_newton_schulz_zero_steps_and_schedule():
     assert rel_fro(u[0], ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("case", ["iid_256x1024", "rank8_256x1024", "iid_300x900", "iid_1024x1024"])
+def test_newton_schulz_polar_express(prec, case):
+    """The Polar Express table (a different triple per step, the first with
+    large coefficients) against the oracle with the same table."""
+    import adamw_optimizer_step_amd as M
+    dt = torch.bfloat16 if prec == "bf16" else torch.float32
+    if case == "rank8_256x1024":
+        g = rank8_plus_noise_256x1024().double()
+        x0 = (g / torch.linalg.matrix_norm(g)).unsqueeze(0).to(dt)
+    else:
+        m, n = (int(v) for v in case.split("_")[1].split("x"))
+        x0 = _x0(2 if m < 1024 else 1, m, n, m + 7 * n, dt)
+    table = list(M.POLAR_EXPRESS)
+    say("ns polar express", prec, case)
+    u = to_np(M.newton_schulz(x0.to(DEV), table, len(table)))
+    xs = to_np(x0).astype(np.float64)
+    for k in range(xs.shape[0]):
+        ref = O.newton_schulz(xs[k], table, "bf16" if prec == "bf16" else "f64", len(table))
+        assert rel_fro(u[k], ref) <= TOL[prec], (k, rel_fro(u[k], ref))
+
+
 # --------------------------------------------------------------------- whole step
 
 def _run_step(groups_np, hp, dts):
@@ -116,8 +138,8 @@ def _check_step(groups_np, dev, mgs, ws, hp, dts, sample=None):
                             coeffs=hp.coeffs, ns_steps=hp.ns_steps, weight_decay=hp.weight_decay,
                             cautious=hp.cautious, equilibrate=hp.equilibrate,
                             precision="bf16" if prec == "bf16" else "f64", param_dtype=dts[0],
-                            mom_dtype=dts[2], norm_eps=hp.norm_eps, eq_eps=hp.eq_eps)
-            # the workspace holds the Newton-Schulz result (before MuonEq POST scaling)
+                            mom_dtype=dts[2], norm_eps=hp.norm_eps, eq_eps=hp.eq_eps, lr_scale=hp.lr_scale)
+            # the workspace holds the Newton-Schulz result (before any row scaling after it)
             u = to_np(M.muon_workspace_update(mgs, hp, ws, gi, k))
             err = rel_fro(u, r["U_ns"])
             assert err <= TOL[prec], f"group {gi} matrix {k}: update error {err:.3e}"
@@ -157,11 +179,7 @@ def test_single_fp32_matrix_256x1024(grad, steps):
     _check_step([(W, G, Mo)], dev, mgs, ws, hp16, dts)
 
 
-@pytest.mark.parametrize("eq", ["off", "pre", "post"])
-@pytest.mark.parametrize("cautious,wd", [(False, 0.0), (True, 0.01)])
-@pytest.mark.parametrize("dts", [("bf16", "bf16", "bf16"), ("f32", "f32", "f32"), ("f32", "bf16", "f32")])
-def test_ragged_groups(eq, cautious, wd, dts):
-    """Ragged, tall, wide, square and degenerate shapes in one call."""
+def _ragged_groups(dts):
     shapes = [(37, 53, 3), (300, 100, 2), (100, 300, 1), (1, 9, 2), (9, 1, 1), (128, 128, 2), (257, 255, 1)]
     rng = np.random.default_rng(77)
     groups_np = []
@@ -176,9 +194,31 @@ def test_ragged_groups(eq, cautious, wd, dts):
         if dts[2] == "bf16":
             Mo = O.round_to_bf16(Mo)
         groups_np.append((W, G, Mo))
+    return groups_np
+
+
+@pytest.mark.parametrize("eq", ["off", "pre", "post", "rms"])
+@pytest.mark.parametrize("cautious,wd", [(False, 0.0), (True, 0.01)])
+@pytest.mark.parametrize("dts", [("bf16", "bf16", "bf16"), ("f32", "f32", "f32"), ("f32", "bf16", "f32")])
+def test_ragged_groups(eq, cautious, wd, dts):
+    """Ragged, tall, wide, square and degenerate shapes in one call."""
+    groups_np = _ragged_groups(dts)
     prec = "f32" if dts[0] == "f32" and dts[2] == "f32" else "bf16"
-    hp = _hp(equilibrate=eq, cautious=cautious, weight_decay=wd, ns_precision=prec)
+    extra = dict(eq_eps=f32r(1e-8), lr_scale="none") if eq == "rms" else {}
+    hp = _hp(equilibrate=eq, cautious=cautious, weight_decay=wd, ns_precision=prec, **extra)
     say("ragged", eq, cautious, wd, dts)
+    dev, mgs, ws = _run_step(groups_np, hp, dts)
+    _check_step(groups_np, dev, mgs, ws, hp, dts)
+
+
+@pytest.mark.parametrize("scale", ["none", "sqrt_max1_r_over_c", "moonshot", "sqrt_max"])
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+def test_lr_scales(scale, prec):
+    """The per-matrix lr multipliers the pages use, on ragged shapes."""
+    dts = ("bf16", "bf16", "bf16") if prec == "bf16" else ("f32", "f32", "f32")
+    groups_np = _ragged_groups(dts)
+    hp = _hp(lr_scale=scale, cautious=True, weight_decay=0.01, ns_precision=prec)
+    say("lr scale", scale, prec)
     dev, mgs, ws = _run_step(groups_np, hp, dts)
     _check_step(groups_np, dev, mgs, ws, hp, dts)
 

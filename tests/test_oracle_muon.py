@@ -329,3 +329,51 @@ def test_full_step_bookkeeping_bf16():
     w2, _ = O.post_stage(W, r["U"], r["c_lr"], r["c_wd"], True)
     assert np.array_equal(r["W"], O.round_to_bf16(w2))
     assert np.array_equal(O.round_to_bf16(r["U"]), r["U"])   # bf16 mode: U holds bf16 values
+
+
+# ---------------------------------------------------------------- scale variants
+
+def test_lr_multiplier_values():
+    # nanochat: x2 for the 4096 x 1024 c_fc, x1 for the 1024 x 4096 c_proj;
+    # Moonshot 0.2 sqrt(max side); sqrt(max side)
+    assert O.lr_multiplier(4096, 1024) == 2.0 and O.lr_multiplier(1024, 4096) == 1.0
+    assert O.lr_multiplier(4096, 1024, "moonshot") == pytest.approx(0.2 * 64)
+    assert O.lr_multiplier(1024, 4096, "sqrt_max") == 64.0
+    assert O.lr_multiplier(7, 3, "none") == 1.0 and O.lr_multiplier(7, 3, False) == 1.0
+    with pytest.raises(ValueError):
+        O.lr_multiplier(2, 2, "bogus")
+
+
+@pytest.mark.parametrize("shape", [(48, 160), (160, 48)])
+@pytest.mark.parametrize("scale,rms", [("moonshot", 0.2), ("sqrt_max", 1.0)])
+def test_scaled_step_rms_of_an_orthogonal_update(shape, scale, rms):
+    # A semi-orthogonal R x C update has Frobenius norm sqrt(min(R, C)), so its
+    # entries' RMS is 1/sqrt(max(R, C)): with Moonshot's 0.2 sqrt(max side) the
+    # step's RMS is 0.2 lr ("Muon vs AdamW, Lion and Sophia: a fair race"),
+    # with sqrt(max side) it is lr ("3.9 Optimizers ...").
+    R, C = shape
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((R, C)) * 0.02).astype(np.float32)
+    G = rng.standard_normal((R, C)).astype(np.float32)
+    Z = np.zeros_like(W)
+    r = O.muon_step(W, G, Z, lr=0.01, coeffs=O.CLASSICAL_QUINTIC, ns_steps=30, precision="f64",
+                    param_dtype="f32", mom_dtype="f32", lr_scale=scale)
+    d = (W.astype(np.float64) - r["W"].astype(np.float64)) / 0.01
+    assert math.sqrt(float(np.mean(d * d))) == pytest.approx(rms, rel=2e-3)
+
+
+def test_normuon_rows_have_rms_lr():
+    # NorMuon ("Chapter 4", section "NorMuon: Normalized Muon"): every row of
+    # the step has RMS lr whatever the spectrum (eps 1e-8 aside)
+    rng = np.random.default_rng(6)
+    R, C = 40, 120
+    W = np.zeros((R, C), np.float32)
+    G = (rng.standard_normal((R, 8)) @ rng.standard_normal((8, C))).astype(np.float32)
+    Z = np.zeros_like(W)
+    r = O.muon_step(W, G, Z, lr=0.01, equilibrate="rms", eq_eps=1e-8, precision="f64", param_dtype="f32",
+                    mom_dtype="f32", lr_scale="none")
+    d = -r["W"].astype(np.float64) / 0.01
+    row_rms = np.sqrt(np.mean(d * d, axis=1))
+    assert np.allclose(row_rms, 1.0, rtol=1e-5)
+    # the row scaling follows the iteration: U_ns is the plain result
+    assert not np.allclose(np.sqrt(np.mean(r["U_ns"].astype(np.float64) ** 2, axis=1)), 1.0, rtol=1e-2)
