@@ -13,8 +13,10 @@ nothing from it. It is written from the pages' statement of the methods:
   "Muon: Orthogonalizing the Update";
 * "Stuck at the optimizer after figuring out backward()" (nanochat discussion,
   reply by mira687): cautious weight decay, MuonEq, the shape lr multiplier;
-* "Muon vs AdamW, Lion and Sophia: a fair race" (mvgpt episode 23), section
-  "Muon": the scalar view of one polynomial step.
+* "Muon vs AdamW, Lion and Sophia: a fair race" (mvgpt episode 23), sections
+  "Muon" (the scalar view of one polynomial step) and "Lion";
+* "3.9 Optimizers", section "Lion: Learning the Sign of the Update" and its
+  exercise 5: the Lion step.
 
 Every function is pinned by tests against values the pages print, closed
 forms, or library routines (see tests/test_oracle_*.py). No function is
@@ -22,6 +24,7 @@ forms, or library routines (see tests/test_oracle_*.py). No function is
 """
 from .bf16 import round_to_bf16, f32_to_bf16_bits, bf16_bits_to_f32  # noqa: F401
 from .adamw import adamw_scalars, adamw_step  # noqa: F401
+from .lion import lion_scalars, lion_step  # noqa: F401
 from .muon import (  # noqa: F401
     KELLER_JORDAN, CLASSICAL_QUINTIC, CUBIC,
     lr_multiplier, momentum_stage, row_sumsq, normalize, newton_schulz,
