@@ -7,5 +7,5 @@ GPU path both take their inputs from this package and share nothing else.
 from .inputs import (  # noqa: F401
     MuonGroupSpec, AdamWSegmentSpec, Workload, WORKLOADS, workload,
     gaussian, kron_spectrum_factors, kron_spectrum_matrix, seed0_gaussian_256x1024,
-    rank8_plus_noise_256x1024, materialize,
+    rank8_plus_noise_256x1024, materialize, grad_factors,
 )

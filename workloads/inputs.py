@@ -270,9 +270,15 @@ def _grad_group(wl: Workload, spec: MuonGroupSpec, gi: int, seed: int, device) -
         return gaussian((n, R, C), wl.grad_rms, seed * 1000 + 17 * gi + 1, device, dt)
     out = torch.empty((n, R, C), device=device, dtype=dt)
     for k in range(n):
-        f = kron_spectrum_factors(R, C, wl.grad_kind, wl.grad_rms, seed * 100003 + 7919 * gi + k)
-        out[k].copy_(kron_spectrum_matrix(f, device=device))
+        out[k].copy_(kron_spectrum_matrix(grad_factors(wl, gi, k, seed), device=device))
     return out
+
+
+def grad_factors(wl: Workload, gi: int, k: int, seed: int = 0):
+    """Singular factors of matrix k of Muon group gi (prescribed-spectrum
+    gradient kinds): the same ones :func:`materialize` builds it from."""
+    spec = wl.muon_groups[gi]
+    return kron_spectrum_factors(spec.rows, spec.cols, wl.grad_kind, wl.grad_rms, seed * 100003 + 7919 * gi + k)
 
 
 def materialize(wl: Workload, device="cpu", seed: int = 0,
