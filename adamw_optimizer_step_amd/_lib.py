@@ -22,7 +22,7 @@ MA_BF16 = 1
 MA_EQ_OFF, MA_EQ_ROWS_PRE, MA_EQ_ROWS_POST, MA_EQ_ROWS_RMS = 0, 1, 2, 3
 MA_SCALE_NONE, MA_SCALE_SQRT_MAX1_R_OVER_C, MA_SCALE_MOONSHOT, MA_SCALE_SQRT_MAX = 0, 1, 2, 3
 MA_MAX_NS_STEPS = 16
-KERNEL_KINDS = ("rownorm", "finalize", "pre", "gram", "poly", "axpy", "post", "adamw")
+KERNEL_KINDS = ("rownorm", "finalize", "pre", "gram", "poly", "axpy", "post", "adamw", "lion")
 MA_WORKSPACE_ALIGN = 256
 
 
@@ -53,6 +53,14 @@ class AdamWSegmentC(C.Structure):
     ]
 
 
+class LionSegmentC(C.Structure):
+    _fields_ = [
+        ("param", C.c_void_p), ("grad", C.c_void_p), ("exp_avg", C.c_void_p), ("n", C.c_int64),
+        ("param_dtype", C.c_int32), ("grad_dtype", C.c_int32), ("lr", C.c_float), ("beta1", C.c_float),
+        ("beta2", C.c_float), ("weight_decay", C.c_float),
+    ]
+
+
 EXPORTS = {
     "ma_muon_workspace_size": (C.c_size_t, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC)]),
     "ma_muon_step": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
@@ -62,6 +70,7 @@ EXPORTS = {
                                            C.POINTER(C.c_int64), C.POINTER(C.c_int32),
                                            C.POINTER(C.c_int32)]),
     "ma_adamw_step": (C.c_int, [C.POINTER(AdamWSegmentC), C.c_int32, C.c_void_p]),
+    "ma_lion_step": (C.c_int, [C.POINTER(LionSegmentC), C.c_int32, C.c_void_p]),
     "ma_status_string": (C.c_char_p, [C.c_int]),
     "ma_last_error": (C.c_char_p, []),
     "ma_version": (C.c_char_p, []),

@@ -184,6 +184,24 @@ def adamw_step(segments: Sequence[dict], stream=None) -> None:
     L.check(L.lib().ma_adamw_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
 
 
+def lion_step(segments: Sequence[dict], stream=None) -> None:
+    """One Lion step. Each segment: param, grad, exp_avg (fp32 tensors,
+    contiguous, equal sizes), lr, beta1, beta2, weight_decay."""
+    if not segments:
+        return
+    arr = (L.LionSegmentC * len(segments))()
+    dev = segments[0]["param"].device
+    for i, s in enumerate(segments):
+        p, g, m = s["param"], s["grad"], s["exp_avg"]
+        for t in (p, g, m):
+            if not t.is_contiguous() or t.numel() != p.numel():
+                raise ValueError("Lion buffers must be contiguous and of equal size")
+        arr[i] = L.LionSegmentC(param=p.data_ptr(), grad=g.data_ptr(), exp_avg=m.data_ptr(), n=p.numel(),
+                                param_dtype=_dt(p), grad_dtype=_dt(g), lr=s["lr"], beta1=s.get("beta1", 0.9),
+                                beta2=s.get("beta2", 0.99), weight_decay=s.get("weight_decay", 0.0))
+    L.check(L.lib().ma_lion_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
+
+
 # ---------------------------------------------------------------------------
 # stage entry points (used by the tests)
 # ---------------------------------------------------------------------------

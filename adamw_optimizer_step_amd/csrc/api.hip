@@ -12,6 +12,7 @@
 
 #include "../../include/muon_adamw.h"
 #include "adamw.hpp"
+#include "lion.hpp"
 #include "muon_elem.hpp"
 #include "ns_gemm.hpp"
 
@@ -586,6 +587,70 @@ int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
     D.eps = S.eps;
     D.decay = S.weight_decay != 0.0f ? 1 : 0;
     D.vec = aligned16(S.param) && aligned16(S.grad) && aligned16(S.exp_avg) && aligned16(S.exp_avg_sq);
+    blocks += nb;
+  }
+  return flush();
+}
+
+int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {
+  if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
+  std::vector<Range> rs;
+  for (int i = 0; i < n; ++i) {
+    const ma_lion_segment& S = segs[i];
+    if (S.n < 0) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0", i);
+    if (S.param_dtype != MA_F32 || S.grad_dtype != MA_F32)
+      return fail(MA_ERR_UNSUPPORTED, "segment %d: Lion buffers must be MA_F32", i);
+    if (S.n == 0) continue;
+    if (!S.param || !S.grad || !S.exp_avg) return fail(MA_ERR_INVALID_ARG, "segment %d: null device pointer", i);
+    if (((uintptr_t)S.param | (uintptr_t)S.grad | (uintptr_t)S.exp_avg) & 3)
+      return fail(MA_ERR_INVALID_ARG, "segment %d: pointer not 4-byte aligned", i);
+    if (!std::isfinite(S.lr) || !std::isfinite(S.weight_decay) || !(S.beta1 >= 0.f && S.beta1 < 1.f) ||
+        !(S.beta2 >= 0.f && S.beta2 < 1.f))
+      return fail(MA_ERR_INVALID_ARG, "segment %d: hyperparameters out of range", i);
+    const uintptr_t nb = (uintptr_t)S.n * 4;
+    rs.push_back({(uintptr_t)S.param, (uintptr_t)S.param + nb, 0});
+    rs.push_back({(uintptr_t)S.grad, (uintptr_t)S.grad + nb, 1});
+    rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, 2});
+  }
+  int rc = check_overlaps(rs);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  LionArgs A{};
+  int64_t blocks = 0;
+  auto flush = [&]() -> int {
+    if (A.nseg == 0) return MA_OK;
+    A.total_blocks = (int32_t)blocks;
+    hipError_t err;
+    {
+      ProfScope ps(MA_K_LION, s);
+      err = launch_lion(A, s);
+    }
+    A = LionArgs{};
+    blocks = 0;
+    return err == hipSuccess ? MA_OK : hip_fail(err, "Lion launch");
+  };
+  for (int i = 0; i < n; ++i) {
+    const ma_lion_segment& S = segs[i];
+    if (S.n == 0) continue;
+    const int64_t nb = (S.n + kLionBlockElems - 1) / kLionBlockElems;
+    if (A.nseg == kMaxLionSegs || blocks + nb > (int64_t)0x7fffffff) {
+      if ((rc = flush())) return rc;
+    }
+    LionSeg& D = A.s[A.nseg++];
+    D.p = reinterpret_cast<float*>(S.param);
+    D.g = reinterpret_cast<const float*>(S.grad);
+    D.m = reinterpret_cast<float*>(S.exp_avg);
+    D.n = S.n;
+    D.block_begin = blocks;
+    const double lr = S.lr, b1 = S.beta1, b2 = S.beta2, wd = S.weight_decay;
+    D.lr = S.lr;
+    D.cd = (float)(1.0 - lr * wd);
+    D.b1 = S.beta1;
+    D.b2 = S.beta2;
+    D.c1 = (float)(1.0 - b1);
+    D.c2 = (float)(1.0 - b2);
+    D.decay = S.weight_decay != 0.0f ? 1 : 0;
+    D.vec = aligned16(S.param) && aligned16(S.grad) && aligned16(S.exp_avg);
     blocks += nb;
   }
   return flush();

@@ -16,7 +16,11 @@
  *   ma_adamw_step  one AdamW step over flat buffers ("3.9 Optimizers: SGD,
  *                  Adam, Adafactor, Lion, Muon & Shampoo", section
  *                  "Implementing AdamW from scratch"; "Chapter 4", section
- *                  "The AdamW Step").
+ *                  "The AdamW Step");
+ *   ma_lion_step   one Lion step over flat buffers ("3.9 Optimizers",
+ *                  section "Lion: Learning the Sign of the Update" and
+ *                  exercise 5; "Muon vs AdamW, Lion and Sophia: a fair
+ *                  race", section "Lion").
  *
  * Conventions for every entry point:
  *   - Pointers named "device" are HIP device pointers; "host" pointers are
@@ -187,6 +191,33 @@ typedef struct {
  * `segments` is a HOST array. */
 int ma_adamw_step(const ma_adamw_segment* segments, int32_t n_segments, void* stream);
 
+/* One flat Lion buffer. param, grad, exp_avg (the momentum, Lion's only
+ * state): DEVICE pointers to n elements each, fp32 (param_dtype and
+ * grad_dtype must be MA_F32), 4-byte aligned. */
+typedef struct {
+  void* param;
+  const void* grad;
+  void* exp_avg;
+  int64_t n;
+  int32_t param_dtype, grad_dtype;
+  float lr, beta1, beta2, weight_decay;
+} ma_lion_segment;
+
+/* One Lion step over every segment (fp32 throughout), per element:
+ *   p = p*(1 - lr*wd)            (only when wd != 0)
+ *   c = beta1*m + (1-beta1)*g    (not stored)
+ *   p = p - lr*sign(c)           sign: +1, -1, +0 for either zero, NaN for NaN
+ *   m = beta2*m + (1-beta2)*g    (after the step, with the raw gradient)
+ * 1 - lr*wd, 1 - beta1 and 1 - beta2 are formed in fp64 on the host and
+ * rounded to fp32 once; each per-element operation is one correctly rounded
+ * fp32 operation (no fused multiply-add). Requirements: finite lr and
+ * weight_decay, 0 <= beta1, beta2 < 1. Segments may be in any order and of
+ * any length (n >= 0); no two buffers, of one segment or of different
+ * segments, may overlap. `segments` is a HOST array. Returns
+ * MA_ERR_INVALID_ARG / MA_ERR_UNSUPPORTED before any launch on a bad
+ * segment. */
+int ma_lion_step(const ma_lion_segment* segments, int32_t n_segments, void* stream);
+
 /* Status text for a code, and the calling thread's last error message. */
 const char* ma_status_string(int status);
 const char* ma_last_error(void);
@@ -212,7 +243,8 @@ typedef enum {
   MA_K_AXPY = 5,      /* X' = a X + B X */
   MA_K_POST = 6,      /* cautious decay and the update */
   MA_K_ADAMW = 7,
-  MA_K_COUNT = 8
+  MA_K_LION = 8,
+  MA_K_COUNT = 9
 } ma_kernel_kind;
 
 int ma_profile_begin(int32_t max_launches);

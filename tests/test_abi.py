@@ -159,6 +159,38 @@ def test_adamw_zero_segments_is_noop():
     assert L.lib().ma_adamw_step(arr, 1, None) == L.MA_OK
 
 
+def lseg(**kw):
+    d = dict(param=BASE, grad=BASE + (1 << 30), exp_avg=BASE + (2 << 30), n=1000, param_dtype=0,
+             grad_dtype=0, lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.0)
+    d.update(kw)
+    return L.LionSegmentC(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), L.MA_ERR_INVALID_ARG),
+    (dict(param_dtype=1), L.MA_ERR_UNSUPPORTED),
+    (dict(grad_dtype=1), L.MA_ERR_UNSUPPORTED),
+    (dict(beta1=1.0), L.MA_ERR_INVALID_ARG),
+    (dict(beta2=-0.1), L.MA_ERR_INVALID_ARG),
+    (dict(beta1=float("nan")), L.MA_ERR_INVALID_ARG),
+    (dict(lr=float("inf")), L.MA_ERR_INVALID_ARG),
+    (dict(weight_decay=float("nan")), L.MA_ERR_INVALID_ARG),
+    (dict(exp_avg=None), L.MA_ERR_INVALID_ARG),
+    (dict(grad=BASE + (1 << 30) + 2), L.MA_ERR_INVALID_ARG),
+    (dict(grad=BASE + 3996), L.MA_ERR_INVALID_ARG),          # overlaps param's last element
+])
+def test_lion_rejects_bad_arguments(kw, code):
+    arr = (L.LionSegmentC * 1)(lseg(**kw))
+    assert L.lib().ma_lion_step(arr, 1, None) == code
+
+
+def test_lion_zero_segments_is_noop():
+    assert L.lib().ma_lion_step(None, 0, None) == L.MA_OK
+    assert L.lib().ma_lion_step(None, -1, None) == L.MA_ERR_INVALID_ARG
+    arr = (L.LionSegmentC * 1)(lseg(n=0, param=None, grad=None, exp_avg=None))
+    assert L.lib().ma_lion_step(arr, 1, None) == L.MA_OK
+
+
 def test_stage_entry_points_validate():
     lib = L.lib()
     assert lib.ma_test_bf16_round(None, None, 10, None) == L.MA_ERR_INVALID_ARG
