@@ -14,11 +14,12 @@
 //
 // Two kernels share the job mapping and the epilogue:
 //  * ns_gemm_dma (bf16): 256 x 256 block tile, 4 waves of 128 x 128 (32x32x16
-//    MFMAs, 16 accumulator blocks per wave). Operand tiles of 256 x 32 move
-//    from global memory straight into a 3-stage LDS ring with
-//    global_load_lds_dwordx4 (no VGPR staging), two tiles ahead of the one
+//    MFMAs, 16 accumulator blocks per wave). Operand tiles of 256 x 64 move
+//    from global memory straight into a 2-stage LDS ring with
+//    global_load_lds_dwordx4 (no VGPR staging), one tile ahead of the one
 //    being multiplied; 16-byte chunks are XOR-swizzled by row so that the
-//    fragment reads are conflict-free.
+//    fragment reads are conflict-free. Blocks are persistent, one per CU,
+//    each walking a fixed share of its XCD's tile list.
 //  * ns_gemm_reg (fp32, and bf16 for small matrices): a register-staged
 //    double-buffered kernel of configurable tile and wave layout.
 // Blocks are dealt to the 8 XCDs so that each XCD gets an eighth of every
@@ -177,6 +178,15 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
           }
         asm volatile("" ::: "memory");
       }
+  }
+  if constexpr (EPI == EPI_POLY && E_DONE) {
+    // the main loop accumulated A A + (b/c) A
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] *= args.c;
   }
 
   T* stg = reinterpret_cast<T*>(smem);
@@ -400,7 +410,7 @@ ns_gemm_reg(const NsArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-DMA kernel (bf16): 256 x 256 x 32 tiles, 4 waves of 128 x 128, a ring of
+// LDS-DMA kernel (bf16): 256 x 256 x BK tiles, 4 waves of 128 x 128, a ring of
 // STAGES k-tiles in LDS
 // ---------------------------------------------------------------------------
 #ifndef MA_DMA_BK
@@ -537,10 +547,11 @@ struct DmaCtx {
 // the next k-step's fragments are read into (na, nb). At the last k-step the
 // next read is of the next tile, after the barrier that also releases this
 // tile's stage to the DMA of tile kt + STAGES.
-// IIB >= 0 (AXPY): this k-tile's values of k are rows of this wave's output
-// blocks IIB + KKI/2, and the Q fragments (X^T rows j) hold X^T[j][i] = X[i][j]
-// for them, so (a I) X^T-block adds the term a*X to the accumulators instead
-// of reading X back in the epilogue.
+// IIB >= 0 (folded term): this k-tile's values of k are rows of this wave's
+// output blocks IIB + KKI/2, and the Q fragments hold Q[j][i] = X[i][j] (AXPY,
+// Q = X^T) or A[i][j] (POLY, A symmetric) for them, so (a I) Q-block adds
+// a*X, or (b/c)*A, to the accumulators instead of reading it back in the
+// epilogue.
 template <int KKI, int IIB>
 __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt, f32x16_t (&acc)[4][4], u32x4_t (&fa)[4],
                                           u32x4_t (&fb)[4], u32x4_t (&na)[4], u32x4_t (&nb)[4]) {
@@ -602,7 +613,12 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt, f32x16_t (&ac
 }
 
 // One output tile: prologue DMA, main loop, epilogue.
-template <int EPI>
+// FOLD: the term that is not a product of the two operands -- a X in AXPY,
+// b A in POLY (as (b/c) A, the epilogue then scaling by c; needs c != 0) --
+// is added inside the main loop by scaled-identity MFMAs against the Q
+// fragments, so the epilogue reads nothing back from global memory. AXPY
+// always folds.
+template <int EPI, bool FOLD>
 __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem) {
   using namespace dma;
   const NsGroup& G = args.g[J.gi];
@@ -624,7 +640,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   c.wm = wave >> 1;
   c.wn = wave & 1;
   c.nk = G.K / BK;   // K is a multiple of 256: nk >= 4
-  c.a = args.a;
+  c.a = EPI == EPI_POLY ? args.b / args.c : args.a;
   const bool isP = wave < 2;
   c.ld_src = isP ? G.ldP : G.ldQ;
   c.src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
@@ -655,9 +671,10 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   u32x4_t f0a[4], f0b[4], f1a[4], f1b[4];
   dma_read_step(smem, 0, lane, c.wm, c.wn, f0a, f0b);
   int kt = 0;
-  if constexpr (EPI == EPI_AXPY) {
+  if constexpr (FOLD) {
     // the k-tiles whose k range is this wave's 128 output rows (K = m_pad,
-    // so they lie inside [0, nk)) carry the a*X term
+    // so they lie inside [0, nk)) carry the a*X (AXPY) or (b/c)*A (POLY)
+    // term: Q rows j hold X^T[j][k] = X[k][j], or A[j][k] = A[k][j]
     const int e_first = (J.bi * BM + c.wm * 128) / BK;
     for (; kt < e_first; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
     if constexpr (BK == 32) {
@@ -672,7 +689,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, EPI == EPI_AXPY>(args, G, J, acc, smem, tid);
+  ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, FOLD>(args, G, J, acc, smem, tid);
 }
 
 // Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
@@ -681,7 +698,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
 // the longest jobs first and, where jobs differ in K, a fixed stride ends
 // about as late as taking jobs on demand would (the blocks holding one long
 // and two short jobs set the end either way).
-template <int EPI>
+template <int EPI, bool FOLD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ns_gemm_dma(const NsArgs args) {
   using namespace dma;
@@ -690,7 +707,7 @@ ns_gemm_dma(const NsArgs args) {
   const int P = (int)(gridDim.x >> 3);
   TileJob J;
   for (int local = (int)(blockIdx.x >> 3); map_job_at(args, x, local, J); local += P) {
-    dma_tile<EPI>(args, J, smem);
+    dma_tile<EPI, FOLD>(args, J, smem);
     __syncthreads();   // the epilogue is done with LDS before the next job's DMA
   }
 }
@@ -715,9 +732,9 @@ static hipError_t launch_reg_epi(int epi, const NsArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int EPI>
+template <int EPI, bool FOLD>
 static hipError_t launch_dma(const NsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((ns_gemm_dma<EPI>), dim3(a.padded_blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD>), dim3(a.padded_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -733,9 +750,10 @@ hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipS
     if (tile.dma) {
       if (tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK) return hipErrorInvalidValue;
       switch (epi) {
-        case EPI_GRAM: return launch_dma<EPI_GRAM>(a, s);
-        case EPI_POLY: return launch_dma<EPI_POLY>(a, s);
-        case EPI_AXPY: return launch_dma<EPI_AXPY>(a, s);
+        case EPI_GRAM: return launch_dma<EPI_GRAM, false>(a, s);
+        case EPI_POLY:
+          return a.c != 0.0f ? launch_dma<EPI_POLY, true>(a, s) : launch_dma<EPI_POLY, false>(a, s);
+        case EPI_AXPY: return launch_dma<EPI_AXPY, true>(a, s);
       }
       return hipErrorInvalidValue;
     }

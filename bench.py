@@ -12,6 +12,8 @@ Prints one JSON line (rank 0). The ``roofline`` object reports the dominant
 kernel (by time) against its roofline, from HIP events recorded around each
 launch on the launch stream during the timed steps; ``cpu_baseline`` times
 the oracle on a bounded sample of the same workload on the host cores.
+``lion`` times ``ma_lion_step`` separately, outside the Muon + AdamW step,
+over fp32 buffers of the AdamW parameters' sizes (20 bytes per element).
 """
 import argparse
 import json
@@ -39,6 +41,7 @@ def parse():
     ap.add_argument("--no-profile", action="store_true", help="time without per-kernel events")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (one captured step replayed --steps times)")
+    ap.add_argument("--no-lion", action="store_true", help="skip the separate Lion step timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed steps, run 3 plain device copies of MIB MiB (read MIB, write MIB) "
                          "as the known-size reference that scales HBM byte counters")
@@ -209,6 +212,7 @@ def main():
                     "unit": r.get("unit"), "frac": round(r.get("achieved", 0) / peak, 4),
                     "traffic": traffic_for(dom, wl.name)}
 
+    lion = None if args.no_lion else lion_timing(M, wl, dev, args.steps)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, T, args.cpu_budget_s)
     out = {
         "metric": "Muon+AdamW full steps/sec at 12L d=1024; NS-GEMM MFMA util %; HBM GB/s",
@@ -240,9 +244,43 @@ def main():
                     "achieved_tflops": round(model["ns_total_flops_per_step"] / (ns_ms * 1e-3) / 1e12, 1) if ns_ms else None,
                     "mfma_util": round(model["ns_total_flops_per_step"] / (ns_ms * 1e-3) / 1e12 / peak_f, 4) if ns_ms else None},
         "kernels": kernels,
+        "lion": lion,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def lion_timing(M, wl, dev, steps):
+    """ma_lion_step over fp32 buffers of the AdamW parameters' sizes (one
+    segment each), timed on its own: warm-up, then ``steps`` launches between
+    two events on the launch stream."""
+    import torch
+    sizes = [a.numel for a in wl.adamw_segments] or [1 << 26]
+    g = torch.Generator(device=dev).manual_seed(5)
+    segs = []
+    for n in sizes:
+        segs.append(dict(param=torch.randn(n, device=dev, generator=g) * 0.02,
+                         grad=torch.randn(n, device=dev, generator=g) * 1e-3,
+                         exp_avg=torch.randn(n, device=dev, generator=g) * 1e-3,
+                         lr=1e-4, beta1=0.95, beta2=0.98, weight_decay=1.0))
+    for _ in range(3):
+        M.lion_step(segs)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        M.lion_step(segs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n = sum(sizes)
+    gbs = 20.0 * n / (ms * 1e-3) / 1e9
+    del segs
+    torch.cuda.empty_cache()
+    return {"elements": n, "segments": len(sizes), "ms_per_step": round(ms, 4),
+            "bytes_per_element": 20, "achieved": round(gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def traffic_for(kernel, workload_name):
@@ -277,19 +315,30 @@ def cpu_baseline(wl, T, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    sample = materialize(wl.scaled(adamw_segments=()), device="cpu", seed=0, max_count=1)
+    # rounds over the shape groups, one more matrix of each group per round,
+    # until the time budget is spent (at least one round)
+    rounds = 16
+    sample = materialize(wl.scaled(adamw_segments=()), device="cpu", seed=0, max_count=rounds)
     spent = 0.0
-    per_group = []
-    for d, g in zip(sample["muon"], wl.muon_groups):
-        W, G, Mo = (d[k][0].float().numpy() for k in ("W", "G", "M"))
-        t0 = time.perf_counter()
-        O.muon_step(W, G, Mo, lr=wl.lr, momentum=wl.momentum, nesterov=wl.nesterov, coeffs=O.KELLER_JORDAN,
-                    ns_steps=T, weight_decay=wl.weight_decay, cautious=wl.cautious, equilibrate=wl.equilibrate,
-                    precision="bf16" if wl.ns_precision == "bf16" else "f64", param_dtype=wl.param_dtype,
-                    mom_dtype=wl.mom_dtype)
-        dt = time.perf_counter() - t0
-        spent += dt
-        per_group.append((g, dt))
+    times = [[] for _ in wl.muon_groups]
+    for r in range(rounds):
+        for gi, d in enumerate(sample["muon"]):
+            if r >= d["W"].shape[0]:
+                continue
+            W, G, Mo = (d[k][r].float().numpy() for k in ("W", "G", "M"))
+            t0 = time.perf_counter()
+            O.muon_step(W, G, Mo, lr=wl.lr, momentum=wl.momentum, nesterov=wl.nesterov,
+                        coeffs=O.KELLER_JORDAN, ns_steps=T, weight_decay=wl.weight_decay, cautious=wl.cautious,
+                        equilibrate=wl.equilibrate, precision="bf16" if wl.ns_precision == "bf16" else "f64",
+                        param_dtype=wl.param_dtype, mom_dtype=wl.mom_dtype)
+            dt = time.perf_counter() - t0
+            spent += dt
+            times[gi].append(dt)
+        if spent >= budget_s:
+            break
+    del sample
+    per_group = [(g, sum(t) / len(t)) for g, t in zip(wl.muon_groups, times)]
+    n_sampled = sum(len(t) for t in times)
     adam_n = min(wl.adamw_numel, 1 << 24)
     adam_s = 0.0
     if adam_n:
@@ -304,9 +353,10 @@ def cpu_baseline(wl, T, budget_s):
     est = sum(g.count * dt for g, dt in per_group) + adam_s * (wl.adamw_numel / max(adam_n, 1))
     return {"value": round(1.0 / est, 6) if est > 0 else None, "unit": "steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"one matrix of each of the {len(per_group)} shape groups through the oracle's full "
-                       f"Muon step ({'bf16 rounding points' if wl.ns_precision == 'bf16' else 'float64'}, "
-                       f"numpy BLAS) and {adam_n} AdamW elements; scaled by matrix and element counts "
+            "sample": (f"{n_sampled} matrices ({', '.join(str(len(t)) for t in times)} of the "
+                       f"{len(per_group)} shape groups) through the oracle's full Muon step "
+                       f"({'bf16 rounding points' if wl.ns_precision == 'bf16' else 'float64'}, numpy BLAS) "
+                       f"and {adam_n} AdamW elements; per-group mean times scaled by matrix and element counts "
                        f"to one whole step ({spent + adam_s:.1f} s of CPU time measured)")}
 
 
