@@ -134,8 +134,12 @@ def muon_workspace_size(groups: Sequence[MuonGroup], hp: MuonHParams) -> int:
 
 
 def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[torch.Tensor] = None,
-              stream=None) -> torch.Tensor:
-    """One Muon step over ``groups`` (in place). Returns the workspace used."""
+              stream=None, stats: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One Muon step over ``groups`` (in place). Returns the workspace used.
+
+    With ``stats`` (contiguous fp32 tensor of at least 2 values per matrix,
+    groups in order), each matrix's ||W_new - W_old||_F and ||W_old||_F are
+    written to it (``ma_muon_step_stats``)."""
     if not groups:
         return workspace
     dev = groups[0].device
@@ -144,8 +148,15 @@ def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     garr, keep = _groups_c(groups)
     h, tab = hp.to_c()
-    L.check(L.lib().ma_muon_step(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
-                                 workspace.numel(), C.c_void_p(_stream(dev, stream))))
+    ws, st = C.c_void_p(workspace.data_ptr()), C.c_void_p(_stream(dev, stream))
+    if stats is None:
+        L.check(L.lib().ma_muon_step(garr, len(groups), C.byref(h), ws, workspace.numel(), st))
+    else:
+        total = sum(g.count for g in groups)
+        if stats.dtype != torch.float32 or not stats.is_contiguous() or stats.numel() < 2 * total:
+            raise ValueError(f"stats must be a contiguous fp32 tensor of at least {2 * total} values")
+        L.check(L.lib().ma_muon_step_stats(garr, len(groups), C.byref(h), ws, workspace.numel(),
+                                           C.c_void_p(stats.data_ptr()), st))
     return workspace
 
 

@@ -95,6 +95,8 @@ struct GroupPlan {
   float c_lr, c_wd;
   int64_t x_stride, a_stride, row_stride;   // elements / floats
   size_t off_x[2], off_xt[2], off_a, off_b, off_rowsq, off_rowf;   // bytes
+  size_t off_part;           // update-norm partial sums: count x ppm_max x 2 floats
+  int ppm_max;
   const ma_muon_group* src;
   // views in the parameter's layout ("direct") and transposed
   size_t off_direct(int buf) const { return tall ? off_xt[buf] : off_x[buf]; }
@@ -132,6 +134,8 @@ void plan_group(GroupPlan& p, int64_t R, int64_t C, int count, int dt_x, size_t&
   p.off_b = off;     off = align_up(off + (size_t)(count * p.a_stride * e), MA_WORKSPACE_ALIGN);
   p.off_rowsq = off; off = align_up(off + (size_t)(count * p.row_stride * 4), MA_WORKSPACE_ALIGN);
   p.off_rowf = off;  off = align_up(off + (size_t)(count * p.row_stride * 4), MA_WORKSPACE_ALIGN);
+  p.ppm_max = post_blocks_per_mat_max(R, C);
+  p.off_part = off;  off = align_up(off + (size_t)count * p.ppm_max * 2 * 4, MA_WORKSPACE_ALIGN);
 }
 
 int validate_hparams(const ma_muon_hparams* hp) {
@@ -430,11 +434,14 @@ size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups, con
   return plan.bytes;
 }
 
-int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
+                   size_t workspace_bytes, float* stats, void* stream) {
   Plan plan;
   int rc = build_plan(groups, n_groups, hp, plan, true);
   if (rc) return rc;
+  int64_t total = 0;
+  for (const GroupPlan& p : plan.g) total += p.count;
   if (plan.bytes > 0) {
     if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is null");
     if ((uintptr_t)workspace % MA_WORKSPACE_ALIGN)
@@ -454,6 +461,7 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
     }
   }
   if (plan.bytes > 0) rs.push_back({(uintptr_t)workspace, (uintptr_t)workspace + plan.bytes, 3});
+  if (stats && total > 0) rs.push_back({(uintptr_t)stats, (uintptr_t)(stats + 2 * total), 3});
   rc = check_overlaps(rs);
   if (rc) return rc;
 
@@ -476,8 +484,9 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
   // 4. T quintic steps
   rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s);
   if (rc) return rc;
-  // 5. (MuonEq POST) and the update
+  // 5. (MuonEq POST) and the update (and the update norms)
   const int ub = hp->ns_steps & 1;
+  int64_t mat0 = 0;   // index of the group's first matrix in `stats`
   for (const GroupPlan& p : plan.g) {
     for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
       const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
@@ -495,11 +504,30 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
       }
       a.tiles_r = (int32_t)((p.R + 63) / 64);
       a.tiles_c = (int32_t)((p.C + 63) / 64);
+      const int ppm = post_blocks_per_mat(a);   // <= p.ppm_max
+      if (stats) a.part = reinterpret_cast<float*>(ws + p.off_part) + (int64_t)first * ppm * 2;
       { ProfScope ps(MA_K_POST, s); err = launch_post(p.dt_p, p.dt_x, a, s); }
       if (err != hipSuccess) return hip_fail(err, "update");
+      if (stats) {
+        err = launch_update_stats(a.part, ppm, cnt, stats + 2 * (mat0 + first), s);
+        if (err != hipSuccess) return hip_fail(err, "update norms");
+      }
     }
+    mat0 += p.count;
   }
   return MA_OK;
+}
+}  // namespace
+
+int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, nullptr, stream);
+}
+
+int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                       void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  if (!stats || ((uintptr_t)stats & 3)) return fail(MA_ERR_INVALID_ARG, "stats is null or not 4-byte aligned");
+  return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, stats, stream);
 }
 
 int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,

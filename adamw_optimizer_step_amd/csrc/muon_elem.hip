@@ -247,6 +247,33 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
   }
 }
 
+// Accumulate the squared change of one weight as stored (W' rounded to the
+// parameter's type) and its squared old value.
+template <int DTP>
+__device__ __forceinline__ void update_sums(float w_old, float w_new, float& sd, float& sw) {
+  const float stored = DTP == DT_BF16 ? bf16_bits_to_f32(f32_to_bf16(w_new)) : w_new;
+  const float d = stored - w_old;
+  sd = __builtin_fmaf(d, d, sd);
+  sw = __builtin_fmaf(w_old, w_old, sw);
+}
+
+// Block-wide sums of (sd, sw) written to out[0..1] (256 threads, all reach it).
+__device__ __forceinline__ void block_sums_out(float sd, float sw, float* out) {
+  __shared__ float red[2][4];
+  sd = wave_sum(sd);
+  sw = wave_sum(sw);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = sd;
+    red[1][wave] = sw;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    out[0] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    out[1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  }
+}
+
 __device__ __forceinline__ float post_elem(float w, float u, float f, bool has_f, const ElemArgs& a) {
   const float ue = has_f ? __fmul_rn(u, f) : u;
   const bool mask = a.cautious ? (__fmul_rn(ue, w) >= 0.0f) : true;
@@ -259,8 +286,9 @@ constexpr int kPostChunks = 4;   // 8-element chunks per thread (vector path)
 // Vector path (C % 8 == 0, 16-byte aligned rows): the matrices' 8-element
 // chunks in row-major order; thread t of block b takes chunks
 // (b*256 + t) + 256*blocks*u... of its matrix, all loads before any update.
-template <int DTP, int DTX>
-__global__ void __launch_bounds__(256) k_post_vec(const ElemArgs a, int blocks_per_mat) {
+// STATS: also the block's sums of (W' - W)^2 and W^2 into a.part.
+template <int DTP, int DTX, bool STATS>
+__device__ __forceinline__ void post_vec_body(const ElemArgs& a, int blocks_per_mat) {
   const int k = blockIdx.x / blocks_per_mat;
   const int b = blockIdx.x - k * blocks_per_mat;
   const uint32_t cpr = (uint32_t)a.C >> 3;                 // chunks per row
@@ -269,6 +297,7 @@ __global__ void __launch_bounds__(256) k_post_vec(const ElemArgs a, int blocks_p
   const void* xd = eptr<DTX>(static_cast<const void*>(a.xd), (int64_t)k * a.x_stride);
   const float* rowf = a.rowf ? a.rowf + (int64_t)k * a.row_stride : nullptr;
   const uint32_t step = (uint32_t)blocks_per_mat * 256u;
+  float sd = 0.0f, sw = 0.0f;   // sums of (W' - W)^2 and W^2 (stored values)
   for (uint32_t q0 = (uint32_t)b * 256u + threadIdx.x; q0 < nch; q0 += step * kPostChunks) {
     float w[kPostChunks][8], u[kPostChunks][8];
     uint32_t rr[kPostChunks], cc[kPostChunks];
@@ -287,16 +316,30 @@ __global__ void __launch_bounds__(256) k_post_vec(const ElemArgs a, int blocks_p
       if (q0 + step * v < nch) {
         const float f = rowf ? rowf[rr[v]] : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[v][e] = post_elem(w[v][e], u[v][e], f, rowf != nullptr, a);
+        for (int e = 0; e < 8; ++e) {
+          const float w0 = w[v][e];
+          w[v][e] = post_elem(w0, u[v][e], f, rowf != nullptr, a);
+          if constexpr (STATS) update_sums<DTP>(w0, w[v][e], sd, sw);
+        }
         store8<DTP>(eptr<DTP>(wp, (int64_t)rr[v] * a.C + cc[v]), w[v]);
       }
     }
   }
+  if constexpr (STATS) block_sums_out(sd, sw, a.part + 2 * (int64_t)blockIdx.x);
+}
+
+template <int DTP, int DTX>
+__global__ void __launch_bounds__(256) k_post_vec(const ElemArgs a, int blocks_per_mat) {
+  post_vec_body<DTP, DTX, false>(a, blocks_per_mat);
+}
+template <int DTP, int DTX>
+__global__ void __launch_bounds__(256) k_post_vec_stats(const ElemArgs a, int blocks_per_mat) {
+  post_vec_body<DTP, DTX, true>(a, blocks_per_mat);
 }
 
 // W <- RNE( (mask ? W - c_wd*W : W) - c_lr*U ), mask = cautious ? (U*W >= 0) : 1.
-template <int DTP, int DTX>
-__global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
+template <int DTP, int DTX, bool STATS>
+__device__ __forceinline__ void post_tile_body(const ElemArgs& a) {
   const int tiles = a.tiles_r * a.tiles_c;
   const int k = blockIdx.x / tiles;
   const int t = blockIdx.x - k * tiles;
@@ -307,6 +350,7 @@ __global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
   const int tid = threadIdx.x;
   const int cl = (tid & 7) * 8;
   const bool vec = a.vec && (a.ld_d & 7) == 0;
+  float sd = 0.0f, sw = 0.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = r0 + (tid >> 3) + 32 * h, c = c0 + cl;
@@ -327,7 +371,11 @@ __global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = post_elem(w[e], u[e], f, a.rowf != nullptr, a);
+    for (int e = 0; e < 8; ++e) {
+      const float w0 = w[e];
+      w[e] = post_elem(w0, u[e], f, a.rowf != nullptr, a);
+      if (STATS && e < n) update_sums<DTP>(w0, w[e], sd, sw);
+    }
     if (vec) {
       store8<DTP>(eptr<DTP>(wp, off), w);
     } else {
@@ -336,6 +384,16 @@ __global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
         if (e < n) store1<DTP>(wp, off + e, w[e]);
     }
   }
+  if constexpr (STATS) block_sums_out(sd, sw, a.part + 2 * (int64_t)blockIdx.x);
+}
+
+template <int DTP, int DTX>
+__global__ void __launch_bounds__(256) k_post(const ElemArgs a) {
+  post_tile_body<DTP, DTX, false>(a);
+}
+template <int DTP, int DTX>
+__global__ void __launch_bounds__(256) k_post_stats(const ElemArgs a) {
+  post_tile_body<DTP, DTX, true>(a);
 }
 
 __global__ void __launch_bounds__(256) k_bf16_round(const float* in, uint16_t* out, int64_t n) {
@@ -391,20 +449,71 @@ hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream
   return hipGetLastError();
 }
 
+// about 4 chunks per thread on the vector path: enough blocks to fill the
+// chip without tiny blocks
+static int post_vec_blocks(int64_t R, int64_t C) {
+  const int64_t nch = R * (C >> 3);
+  const int64_t bpm = (nch + 256 * kPostChunks - 1) / (256 * kPostChunks);
+  return bpm < 1 ? 1 : (int)bpm;
+}
+
+static bool post_uses_vec(const ElemArgs& a) { return a.vec && (a.C & 7) == 0 && (a.ld_d & 7) == 0; }
+
+int post_blocks_per_mat(const ElemArgs& a) {
+  return post_uses_vec(a) ? post_vec_blocks(a.R, a.C) : a.tiles_r * a.tiles_c;
+}
+
+int post_blocks_per_mat_max(int64_t R, int64_t C) {
+  const int tiles = (int)(((R + 63) / 64) * ((C + 63) / 64));
+  const int vecb = (C & 7) == 0 ? post_vec_blocks(R, C) : 0;
+  return tiles > vecb ? tiles : vecb;
+}
+
 hipError_t launch_post(int dt_p, int dt_x, const ElemArgs& a, hipStream_t s) {
   if (a.count <= 0 || a.R <= 0 || a.C <= 0) return hipSuccess;
-  if (a.vec && (a.C & 7) == 0 && (a.ld_d & 7) == 0) {
-    // about 4 chunks per thread: enough blocks to fill the chip without tiny blocks
-    const int64_t nch = (int64_t)a.R * (a.C >> 3);
-    int64_t bpm = (nch + 256 * kPostChunks - 1) / (256 * kPostChunks);
-    if (bpm < 1) bpm = 1;
-    const int bpm_i = (int)bpm;
-    MA_DISPATCH2(dt_p, dt_x, k_post_vec, dim3(a.count * bpm_i), dim3(256), 0, s, a, bpm_i);
+  const int bpm = post_blocks_per_mat(a);
+  if (post_uses_vec(a)) {
+    if (a.part) MA_DISPATCH2(dt_p, dt_x, k_post_vec_stats, dim3(a.count * bpm), dim3(256), 0, s, a, bpm);
+    else MA_DISPATCH2(dt_p, dt_x, k_post_vec, dim3(a.count * bpm), dim3(256), 0, s, a, bpm);
     return hipGetLastError();
   }
-  const int blocks = a.count * a.tiles_r * a.tiles_c;
-  if (blocks <= 0) return hipSuccess;
-  MA_DISPATCH2(dt_p, dt_x, k_post, dim3(blocks), dim3(256), 0, s, a);
+  if (a.count * bpm <= 0) return hipSuccess;
+  if (a.part) MA_DISPATCH2(dt_p, dt_x, k_post_stats, dim3(a.count * bpm), dim3(256), 0, s, a);
+  else MA_DISPATCH2(dt_p, dt_x, k_post, dim3(a.count * bpm), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// One block per matrix: the two sums over its ppm partials in fp64, each
+// thread taking a fixed stride and the block reducing in a fixed tree, so the
+// result does not depend on timing.
+__global__ void __launch_bounds__(256) k_update_stats(const float* part, int ppm, float* out) {
+  __shared__ double red[2][256];
+  const int k = blockIdx.x;
+  const float* p = part + 2 * (int64_t)k * ppm;
+  double sd = 0.0, sw = 0.0;
+  for (int b = threadIdx.x; b < ppm; b += 256) {
+    sd += (double)p[2 * b];
+    sw += (double)p[2 * b + 1];
+  }
+  red[0][threadIdx.x] = sd;
+  red[1][threadIdx.x] = sw;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + h];
+      red[1][threadIdx.x] += red[1][threadIdx.x + h];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[2 * k] = (float)sqrt(red[0][0]);
+    out[2 * k + 1] = (float)sqrt(red[1][0]);
+  }
+}
+
+hipError_t launch_update_stats(const float* part, int ppm, int count, float* out, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_update_stats, dim3(count), dim3(256), 0, s, part, ppm, out);
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct ElemArgs {
   int32_t finalize_mode;     // 0: Frobenius only, 1: MuonEq pre, 2: MuonEq post
   int32_t vec;               // C % 8 == 0 and every matrix pointer 16-byte aligned
   int32_t pure_copy;         // k_pre: X0 = G (no momentum; M untouched)
+  float* part;               // k_post: per-block (sum (W'-W)^2, sum W^2), 2 floats per block, or null
   MatPtr mat[kMaxMatsPerLaunch];
 };
 
@@ -40,6 +41,13 @@ hipError_t launch_rowsumsq_buffer(int dt_x, const ElemArgs& a, hipStream_t s);
 hipError_t launch_finalize(const ElemArgs& a, hipStream_t s);
 hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s);
 hipError_t launch_post(int dt_p, int dt_x, const ElemArgs& a, hipStream_t s);
+// blocks per matrix of the launch_post call for `a` (the partial sums it writes)
+int post_blocks_per_mat(const ElemArgs& a);
+// at most this many, whatever the matrices' alignment (workspace sizing)
+int post_blocks_per_mat_max(int64_t R, int64_t C);
+// out[2k] = sqrt(sum of part[2(k*ppm + b)]), out[2k+1] = sqrt(sum of part[2(k*ppm + b) + 1]),
+// b < ppm, summed in a fixed order in fp64, for k < count
+hipError_t launch_update_stats(const float* part, int ppm, int count, float* out, hipStream_t s);
 hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 
 }  // namespace ma

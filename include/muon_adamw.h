@@ -129,7 +129,8 @@ typedef struct {
 /* Bytes of device workspace ma_muon_step needs for these groups and
  * hyperparameters (0 on invalid arguments; see ma_last_error). The
  * workspace holds the normalised momentum and the Newton-Schulz iterates
- * and Gram matrices of every matrix, padded to multiples of 256. */
+ * and Gram matrices of every matrix, padded to multiples of 256, and the
+ * partial sums of ma_muon_step_stats. */
 size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
                               const ma_muon_hparams* hp);
 
@@ -152,6 +153,21 @@ size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
  * the pointers passed). */
 int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ma_muon_step that also reports, per matrix, the size of the step it took:
+ * the per-layer ratio ||delta theta|| / ||theta|| that "3.9 Optimizers: SGD,
+ * Adam, Adafactor, Lion, Muon & Shampoo" (section "Large-batch training:
+ * LARS, LAMB and the trust ratio") recommends logging. stats: DEVICE array of
+ * 2 floats per matrix, groups in order and matrices in order within a group:
+ *   stats[2k]   = ||W_new - W_old||_F, W_new as stored (after rounding to
+ *                 param_dtype), W_old the weight before the step
+ *   stats[2k+1] = ||W_old||_F
+ * Per-element squares are summed in fp32 per block and the block sums in
+ * fp64 in a fixed order, so the result is deterministic. stats must be
+ * 4-byte aligned and must not overlap any other buffer (MA_ERR_INVALID_ARG).
+ * The update itself is identical to ma_muon_step's. */
+int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                       void* workspace, size_t workspace_bytes, float* stats, void* stream);
 
 /* Where matrix `index` of group `group` keeps the result of its Newton-Schulz
  * iteration inside a workspace after ma_muon_step (for inspection; valid

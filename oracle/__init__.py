@@ -28,5 +28,5 @@ from .lion import lion_scalars, lion_step  # noqa: F401
 from .muon import (  # noqa: F401
     KELLER_JORDAN, CLASSICAL_QUINTIC, CUBIC,
     lr_multiplier, momentum_stage, row_sumsq, normalize, newton_schulz,
-    post_stage, muon_step, scalar_polynomial, polar_svd, polar_eigh,
+    post_stage, muon_step, scalar_polynomial, polar_svd, polar_eigh, update_norms,
 )

@@ -267,6 +267,18 @@ def scalar_polynomial(s, coeffs, ns_steps=None):
     return s
 
 
+def update_norms(w_old, w_new):
+    """``(||w_new - w_old||_F, ||w_old||_F)`` in float64: the size of one step
+    and of the weight it was taken from, whose ratio is the per-layer
+    diagnostic of "3.9 Optimizers ...", section "Large-batch training: LARS,
+    LAMB and the trust ratio". Both arrays hold the stored values (w_new
+    after rounding to the parameter's type)."""
+    a = np.asarray(w_old, dtype=f64)
+    b = np.asarray(w_new, dtype=f64)
+    d = b - a
+    return math.sqrt(float(np.sum(d * d))), math.sqrt(float(np.sum(a * a)))
+
+
 def polar_svd(M):
     """Exact polar factor ``U V^T`` from the thin SVD (singular values set to 1).
 

@@ -129,6 +129,18 @@ def test_muon_step_rejects_overlaps():
     assert call_step(g, h, ws=p[1] - 256) == L.MA_ERR_INVALID_ARG   # workspace over a weight
 
 
+def test_muon_step_stats_validates_stats_pointer():
+    g, (p, gg, m) = group(rows=64, cols=128)
+    h, tab = hp()
+    arr = (L.MuonGroupC * 1)(g)
+    lib = L.lib()
+    call = lambda st: lib.ma_muon_step_stats(arr, 1, C.byref(h), C.c_void_p(BASE * 4), 1 << 40, st, None)
+    assert call(None) == L.MA_ERR_INVALID_ARG                          # null
+    assert call(C.c_void_p(BASE * 8 + 2)) == L.MA_ERR_INVALID_ARG      # not 4-byte aligned
+    assert call(C.c_void_p(p[0] + 64)) == L.MA_ERR_INVALID_ARG         # overlaps a weight
+    assert call(C.c_void_p(BASE * 4 + 512)) == L.MA_ERR_INVALID_ARG    # inside the workspace
+
+
 def seg(**kw):
     d = dict(param=BASE, grad=BASE + (1 << 30), exp_avg=BASE + (2 << 30), exp_avg_sq=BASE + (3 << 30),
              n=1000, param_dtype=0, grad_dtype=0, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,

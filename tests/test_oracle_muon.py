@@ -377,3 +377,31 @@ def test_normuon_rows_have_rms_lr():
     assert np.allclose(row_rms, 1.0, rtol=1e-5)
     # the row scaling follows the iteration: U_ns is the plain result
     assert not np.allclose(np.sqrt(np.mean(r["U_ns"].astype(np.float64) ** 2, axis=1)), 1.0, rtol=1e-2)
+
+
+def test_update_norms_hand_case():
+    # step [[0, 1], [2, 0]] from a weight of norm 5 (3-4-5): sizes sqrt(5) and 5
+    d, w = O.update_norms([[3.0, 0.0], [0.0, 4.0]], [[3.0, 1.0], [2.0, 4.0]])
+    assert d == math.sqrt(5.0) and w == 5.0
+
+
+def test_update_norms_pure_decay_ratio_is_the_decay():
+    # w_new = (1 - c) w with c = 2^-7 and dyadic w: every product is exact, so
+    # the ratio ||delta|| / ||w|| is exactly c
+    rng = np.random.default_rng(4)
+    w = (rng.integers(-512, 513, (64, 96)) / 256.0).astype(np.float32)
+    c = 2.0 ** -7
+    d, n = O.update_norms(w, (w * np.float32(1.0 - c)).astype(np.float32))
+    assert abs(d / n - c) <= 1e-15
+
+
+def test_update_norms_orthogonal_step():
+    # a step on entries where the weight is zero: ||w_new||^2 = ||w||^2 + ||delta||^2
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((32, 32))
+    w[:, 16:] = 0.0
+    step = np.zeros_like(w)
+    step[:, 16:] = rng.standard_normal((32, 16))
+    d, n = O.update_norms(w, w + step)
+    n_new, _ = O.update_norms(np.zeros_like(w), w + step)
+    assert abs(n_new ** 2 - (n ** 2 + d ** 2)) <= 1e-12 * n_new ** 2
