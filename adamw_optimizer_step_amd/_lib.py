@@ -79,6 +79,7 @@ EXPORTS = {
     "ma_profile_begin": (C.c_int, [C.c_int32]),
     "ma_profile_end": (C.c_int, []),
     "ma_profile_read": (C.c_int, [C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
+    "ma_calib_mfma": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "ma_test_bf16_round": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
     "ma_test_muon_momentum": (C.c_int, [C.POINTER(MuonGroupC), C.c_float, C.c_int32, C.c_void_p,
                                         C.c_void_p]),

@@ -13,6 +13,7 @@
 #include "../../include/muon_adamw.h"
 #include "adamw.hpp"
 #include "lion.hpp"
+#include "calib.hpp"
 #include "muon_elem.hpp"
 #include "ns_gemm.hpp"
 
@@ -682,6 +683,16 @@ int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {
     blocks += nb;
   }
   return flush();
+}
+
+// ---------------------------------------------------------------------------
+// calibration
+// ---------------------------------------------------------------------------
+int ma_calib_mfma(int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !sink || ((uintptr_t)sink & 3))
+    return fail(MA_ERR_INVALID_ARG, "blocks and iters must be > 0 and sink a 4-byte aligned pointer");
+  hipError_t err = launch_calib_mfma(blocks, iters, sink, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MA_OK : hip_fail(err, "calibration launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -14,6 +14,9 @@ launch on the launch stream during the timed steps; ``cpu_baseline`` times
 the oracle on a bounded sample of the same workload on the host cores.
 ``lion`` times ``ma_lion_step`` separately, outside the Muon + AdamW step,
 over fp32 buffers of the AdamW parameters' sizes (20 bytes per element).
+``practical_peaks`` measures what the part sustains with the simplest
+kernels (an MFMA loop with no memory traffic, a plain copy), beside the spec
+peaks the roofline uses.
 """
 import argparse
 import json
@@ -138,17 +141,20 @@ def main():
     if profile:
         L.check(lib.ma_profile_begin(args.steps * 64 + 64))
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event at every step boundary: the whole-run mean and the per-step spread
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
+    marks[0].record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
-    e1.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     if profile:
         L.check(lib.ma_profile_end())
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
     ms_eager = ms
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     # The same step captured once in a HIP graph and replayed: the kernels
@@ -213,6 +219,11 @@ def main():
                     "traffic": traffic_for(dom, wl.name)}
 
     lion = None if args.no_lion else lion_timing(M, wl, dev, args.steps)
+    practical = practical_peaks(L, lib, dev)
+    if roofline is not None and practical:
+        key = "mfma_bf16" if roofline["bound"] == "mfma" else "copy"
+        if roofline["unit"] == practical[key]["unit"] and roofline.get("achieved"):
+            roofline["frac_of_practical_peak"] = round(roofline["achieved"] / practical[key]["achieved"], 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, T, args.cpu_budget_s)
     out = {
         "metric": "Muon+AdamW full steps/sec at 12L d=1024; NS-GEMM MFMA util %; HBM GB/s",
@@ -235,6 +246,7 @@ def main():
                    "timing": ("HIP-graph replay of one captured step" if ms_graph is not None and ms == ms_graph
                               else "eager launches"),
                    "ms_per_step_eager": round(ms_eager, 4),
+                   "eager_step_ms_p10_median_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
                    "ms_per_step_graph": round(ms_graph, 4) if ms_graph is not None else None,
                    "kernel_timing": "per-kernel HIP events inside the eager timed steps" if profile
                    else "no per-kernel events"},
@@ -245,9 +257,48 @@ def main():
                     "mfma_util": round(model["ns_total_flops_per_step"] / (ns_ms * 1e-3) / 1e12 / peak_f, 4) if ns_ms else None},
         "kernels": kernels,
         "lion": lion,
+        "practical_peaks": practical,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def practical_peaks(L, lib, dev):
+    """What this part sustains with the simplest kernels, beside the spec peaks:
+    bf16 MFMA with no memory traffic (ma_calib_mfma: 1024 workgroups of 4
+    waves, each wave 16 independent 32x32x16 MFMAs per round), and a plain
+    1 GiB fp32 copy (torch.neg: 1 GiB read, 1 GiB written)."""
+    import ctypes as C
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    blocks, iters = 1024, 2048
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L.check(lib.ma_calib_mfma(blocks, iters, C.c_void_p(sink.data_ptr()), C.c_void_p(stream.cuda_stream)))
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        L.check(lib.ma_calib_mfma(blocks, iters, C.c_void_p(sink.data_ptr()), C.c_void_p(stream.cuda_stream)))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mfma_tf = 3 * blocks * 4 * iters * 16 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        torch.neg(src, out=dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 8 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"mfma_bf16": {"achieved": round(mfma_tf, 1), "unit": "TFLOP/s", "kernel": "ma_calib_mfma",
+                          "frac_of_spec": round(mfma_tf / PEAK_BF16_TFLOPS, 4)},
+            "copy": {"achieved": round(copy_gbs, 1), "unit": "GB/s", "kernel": "torch.neg over 1 GiB fp32",
+                     "frac_of_spec": round(copy_gbs / PEAK_HBM_GBS, 4)}}
 
 
 def lion_timing(M, wl, dev, steps):

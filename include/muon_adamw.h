@@ -268,6 +268,16 @@ int ma_profile_end(void);
 int ma_profile_read(int32_t kind, double* total_ms, int64_t* launches);
 
 /* ---------------------------------------------------------------------------
+ * Calibration (not part of the optimizer step): the bf16 MFMA rate the part
+ * sustains without memory traffic, the practical ceiling the Newton-Schulz
+ * GEMMs are compared with. Launches `blocks` workgroups of 4 waves; each
+ * wave issues iters x 16 independent 32x32x16 bf16 MFMAs (32768 flops each)
+ * on register operands and stores one float per lane into sink (DEVICE,
+ * blocks x 256 floats, 4-byte aligned). Time it with events on `stream`.
+ * ------------------------------------------------------------------------- */
+int ma_calib_mfma(int32_t blocks, int32_t iters, float* sink, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Stage entry points, used by the test suite to check single stages with
  * identical inputs on both sides. Same conventions as above.
  * ------------------------------------------------------------------------- */

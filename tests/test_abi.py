@@ -217,3 +217,11 @@ def test_hparams_table():
     with pytest.raises(ValueError):
         MuonHParams(ns_steps=2, coeffs=[(1, 0, 0)] * 3).table()
     assert MuonHParams(ns_steps=2, coeffs=[(1, 0, 0), (2, 0, 0)]).table() == [1, 0, 0, 2, 0, 0]
+
+
+def test_calib_mfma_validates():
+    lib = L.lib()
+    assert lib.ma_calib_mfma(0, 10, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 0, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 10, None, None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 10, C.c_void_p(BASE + 2), None) == L.MA_ERR_INVALID_ARG
