@@ -72,6 +72,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 NsTile parse_tile(const char* env, NsTile d) {
   if (const char* e = getenv(env)) {
     if (strcmp(e, "dma") == 0) return {256, 256, ns_dma_bk(), 2, 2, 1};
+    if (strcmp(e, "dma8") == 0) return {256, 256, ns_dma_bk(), 2, 4, 1};
     NsTile x{};
     if (sscanf(e, "%dx%dx%d:%dx%d", &x.bm, &x.bn, &x.bk, &x.wgm, &x.wgn) == 5) return x;
   }
@@ -80,8 +81,10 @@ NsTile parse_tile(const char* env, NsTile d) {
 
 NsTile ns_tile(int dtype, bool symmetric) {
   if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
-  static const NsTile axpy = parse_tile("MA_NS_TILE", {256, 256, ns_dma_bk(), 2, 2, 1});
-  static const NsTile sym = parse_tile("MA_NS_TILE_SYM", {256, 256, ns_dma_bk(), 2, 2, 1});
+  // the LDS-DMA kernel with 8 waves (2 x 4 of 128 x 64, two per SIMD); "dma"
+  // selects the 4-wave form (2 x 2 of 128 x 128)
+  static const NsTile axpy = parse_tile("MA_NS_TILE", {256, 256, ns_dma_bk(), 2, 4, 1});
+  static const NsTile sym = parse_tile("MA_NS_TILE_SYM", {256, 256, ns_dma_bk(), 2, 4, 1});
   return symmetric ? sym : axpy;
 }
 

@@ -410,8 +410,10 @@ ns_gemm_reg(const NsArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-DMA kernel (bf16): 256 x 256 x BK tiles, 4 waves of 128 x 128, a ring of
-// STAGES k-tiles in LDS
+// LDS-DMA kernel (bf16): 256 x 256 x BK tiles, WGM x WGN waves (2 x 2 of
+// 128 x 128, one wave per SIMD; or 2 x 4 of 128 x 64, two waves per SIMD so
+// that one wave's fragment reads and waits overlap the other's MFMAs), a ring
+// of STAGES k-tiles in LDS
 // ---------------------------------------------------------------------------
 #ifndef MA_DMA_BK
 #define MA_DMA_BK 64
@@ -429,10 +431,21 @@ constexpr int STAGE_BYTES = (BM + BN) * ROWB;     // P rows 0..255, Q rows 256..
 constexpr int MAIN = STAGES * STAGE_BYTES;
 constexpr int EPI = EpiSmem<DT_BF16, BM, BN>::BYTES;
 constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
-constexpr int DMA_PER_WAVE = STAGE_BYTES / 4 / 1024;   // each wave fills a quarter
 static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
 static_assert(STAGES >= 2 && BYTES <= 160 * 1024, "LDS ring must fit in 160 KiB");
-static_assert((STAGES - 1) * DMA_PER_WAVE <= 63, "vmcnt range");
+// per wave-grid sizes: wave sub-tile WTM x WTN of FM x FN 32x32 blocks; each
+// wave fills PANEL consecutive stage rows with DPW 1 KiB DMA instructions
+template <int WGM, int WGN>
+struct Grid {
+  static constexpr int NW = WGM * WGN;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int PANEL = (BM + BN) / NW;
+  static constexpr int DPW = STAGE_BYTES / NW / 1024;
+  static_assert((STAGES - 1) * DPW <= 63, "vmcnt range");
+  static_assert(WTM == 128, "the folded term covers 128 output rows per wave");
+  static_assert(PANEL % 64 == 0 && BM % PANEL == 0, "panels start at multiples of 64 rows, inside P or Q");
+};
 // Row r's logical 16-byte chunk c is stored at physical chunk c ^ swz(r).
 // An LDS cycle serves 16 lanes of a ds_read_b128: rows r..r+15 (r a
 // multiple of 16) at one logical chunk. Rows repeat the 64-bank pattern
@@ -448,46 +461,51 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define MA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
 // wait until at most `tiles` k-tile DMAs of this wave are outstanding
+template <int DPW>
 __device__ __forceinline__ void dma_wait_tiles(int tiles) {
   using namespace dma;
   switch (tiles) {
     case 0: MA_WAIT_VMCNT(0); break;
-    case 1: MA_WAIT_VMCNT(1 * DMA_PER_WAVE); break;
-    case 2: MA_WAIT_VMCNT((STAGES > 2 ? 2 : 1) * DMA_PER_WAVE); break;
-    case 3: MA_WAIT_VMCNT((STAGES > 3 ? 3 : 1) * DMA_PER_WAVE); break;
-    default: MA_WAIT_VMCNT((STAGES > 4 ? 4 : 1) * DMA_PER_WAVE); break;
+    case 1: MA_WAIT_VMCNT(1 * DPW); break;
+    case 2: MA_WAIT_VMCNT((STAGES > 2 ? 2 : 1) * DPW); break;
+    case 3: MA_WAIT_VMCNT((STAGES > 3 ? 3 : 1) * DPW); break;
+    default: MA_WAIT_VMCNT((STAGES > 4 ? 4 : 1) * DPW); break;
   }
 }
 
 // Fragment reads of MFMA k-step kk (16 values of k) of a k-tile: this wave's
-// four 32-row blocks of P (fa) and of Q (fb); lane (l32, lh) reads row l32
+// FM 32-row blocks of P (fa) and FN of Q (fb); lane (l32, lh) reads row l32
 // of each block at logical chunk 2 kk + lh.
+template <int WGM, int WGN>
 __device__ __forceinline__ void dma_read_step(const unsigned char* cur, int kk, int lane, int wm, int wn,
-                                              u32x4_t (&fa)[4], u32x4_t (&fb)[4]) {
+                                              u32x4_t (&fa)[dma::Grid<WGM, WGN>::FM],
+                                              u32x4_t (&fb)[dma::Grid<WGM, WGN>::FN]) {
   using namespace dma;
+  using Gd = Grid<WGM, WGN>;
   const int l32 = lane & 31, c = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wm * 128 + i * 32 + l32;
+  for (int i = 0; i < Gd::FM; ++i) {
+    const int r = wm * Gd::WTM + i * 32 + l32;
     fa[i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = BM + wn * 128 + j * 32 + l32;
+  for (int j = 0; j < Gd::FN; ++j) {
+    const int r = BM + wn * Gd::WTN + j * 32 + l32;
     fb[j] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
   }
 }
 
-// This wave's DMA of one k-tile (a quarter of the stage: rows
-// [w*128, w*128+128) of P or Q) into `fill`. Instruction q covers rows
+// This wave's DMA of one k-tile (its panel of the stage: PANEL rows of P or
+// Q) into `fill`. Instruction q covers rows
 // q*RPI .. q*RPI+RPI-1 of the wave's panel; lane i lands at byte 1024 q + 16 i
 // (row q*RPI + i/CPR, physical chunk i%CPR) and so loads logical chunk
 // (i%CPR) ^ swz(row) from memory: lane_off[q & 1] holds that offset.
+template <int DPW>
 __device__ __forceinline__ void dma_issue(unsigned char* fill, const uint16_t* src, int ld_src,
                                           const int (&lane_off)[2], int k0) {
   using namespace dma;
 #pragma unroll
-  for (int q = 0; q < DMA_PER_WAVE; ++q)
+  for (int q = 0; q < DPW; ++q)
     __builtin_amdgcn_global_load_lds(src + (int64_t)(q * RPI) * ld_src + lane_off[q & 1] + k0,
                                      (lds_void_t*)(fill + q * 1024), 16, 0, 0);
 }
@@ -501,19 +519,19 @@ __device__ __forceinline__ void dma_issue_one(unsigned char* fill, const uint16_
 }
 
 // MFMAs of one k-step for accumulator rows [I0, I1)
-template <int I0, int I1>
-__device__ __forceinline__ void mfma_rows(f32x16_t (&acc)[4][4], const u32x4_t (&fa)[4], const u32x4_t (&fb)[4]) {
+template <int I0, int I1, int FM, int FN>
+__device__ __forceinline__ void mfma_rows(f32x16_t (&acc)[FM][FN], const u32x4_t (&fa)[FM], const u32x4_t (&fb)[FN]) {
 #pragma unroll
   for (int i = I0; i < I1; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mfma_frag<DT_BF16>(acc[i][j], fa[i], fb[j]);
+    for (int j = 0; j < FN; ++j) mfma_frag<DT_BF16>(acc[i][j], fa[i], fb[j]);
 }
 
 // acc[II][j] += (a I) X^T-block for k-step h (0 or 1) of row block II, with
 // a = a_hi + a_lo (both exact in bf16). Lane (l32, lh) holds k = 16 h + 8 lh + e
 // of the block, and row i = l32 of a I is nonzero only at k = i.
-template <int II>
-__device__ __forceinline__ void ident_step(f32x16_t (&acc)[4][4], const u32x4_t (&fb)[4], int h, int lane,
+template <int II, int FM, int FN>
+__device__ __forceinline__ void ident_step(f32x16_t (&acc)[FM][FN], const u32x4_t (&fb)[FN], int h, int lane,
                                            float a_coef) {
   const int l32 = lane & 31, lh = lane >> 5;
   const float a_hi = __builtin_bit_cast(float, __float_as_uint(a_coef) & 0xFFFF0000u);
@@ -528,7 +546,7 @@ __device__ __forceinline__ void ident_step(f32x16_t (&acc)[4][4], const u32x4_t 
     id_lo[w] = (e == 2 * w ? lo16 : 0u) | (e == 2 * w + 1 ? lo16 << 16 : 0u);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < FN; ++j) {
     mfma_frag<DT_BF16>(acc[II][j], id_hi, fb[j]);
     mfma_frag<DT_BF16>(acc[II][j], id_lo, fb[j]);
   }
@@ -552,19 +570,23 @@ struct DmaCtx {
 // Q = X^T) or A[i][j] (POLY, A symmetric) for them, so (a I) Q-block adds
 // a*X, or (b/c)*A, to the accumulators instead of reading it back in the
 // epilogue.
-template <int KKI, int IIB>
-__device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt, f32x16_t (&acc)[4][4], u32x4_t (&fa)[4],
-                                          u32x4_t (&fb)[4], u32x4_t (&na)[4], u32x4_t (&nb)[4]) {
+template <int KKI, int IIB, int WGM, int WGN>
+__device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
+                                          f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
+                                          u32x4_t (&fa)[dma::Grid<WGM, WGN>::FM], u32x4_t (&fb)[dma::Grid<WGM, WGN>::FN],
+                                          u32x4_t (&na)[dma::Grid<WGM, WGN>::FM], u32x4_t (&nb)[dma::Grid<WGM, WGN>::FN]) {
   using namespace dma;
+  using Gd = Grid<WGM, WGN>;
+  constexpr int FM = Gd::FM, FN = Gd::FN, DPW = Gd::DPW;
   const int s_cur = kt % STAGES;
   if constexpr (KKI + 1 < KK) {
     // the first row block goes before the reads, so that the wait for (fa, fb)
     // (read during the previous k-step) is not also a wait for the new reads
     mfma_rows<0, 1>(acc, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
-    dma_read_step(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
+    dma_read_step<WGM, WGN>(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_rows<1, 4>(acc, fa, fb);
+    mfma_rows<1, FM>(acc, fa, fb);
   } else {
     // this wave's reads of tile kt are complete (on every path, so that the
     // MFMAs below need no wait for them)
@@ -575,9 +597,9 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt, f32x16_t (&ac
       // the barrier every wave has read all of tile kt, so its stage may be
       // refilled with tile kt+STAGES
       const int later = c.nk - 2 - kt;
-      dma_wait_tiles(later < STAGES - 2 ? later : STAGES - 2);
+      dma_wait_tiles<DPW>(later < STAGES - 2 ? later : STAGES - 2);
       __builtin_amdgcn_s_barrier();
-      dma_read_step(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
+      dma_read_step<WGM, WGN>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
     }
     __builtin_amdgcn_sched_barrier(0);
     // the DMA of tile kt+STAGES into the stage just released, one instruction
@@ -587,10 +609,10 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt, f32x16_t (&ac
     unsigned char* fill_at = c.wave_fill + s_cur * STAGE_BYTES;
     const int k0 = (kt + STAGES) * BK;
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      mfma_frag<DT_BF16>(acc[idx / 4][idx % 4], fa[idx / 4], fb[idx % 4]);
+    for (int idx = 0; idx < FM * FN; ++idx) {
+      mfma_frag<DT_BF16>(acc[idx / FN][idx % FN], fa[idx / FN], fb[idx % FN]);
 #pragma unroll
-      for (int q = idx * DMA_PER_WAVE / 16; q < (idx + 1) * DMA_PER_WAVE / 16; ++q)
+      for (int q = idx * DPW / (FM * FN); q < (idx + 1) * DPW / (FM * FN); ++q)
         if (fill) dma_issue_one(fill_at, c.src, c.ld_src, c.lane_off, k0, q);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -601,14 +623,16 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt, f32x16_t (&ac
 
 // One k-tile: KK k-steps, the fragment sets alternating (0, 1) -> (1, 0) -> ...
 // so that (f0a, f0b) again hold the next tile's first k-step afterwards.
-template <int IIB>
-__device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt, f32x16_t (&acc)[4][4], u32x4_t (&f0a)[4],
-                                          u32x4_t (&f0b)[4], u32x4_t (&f1a)[4], u32x4_t (&f1b)[4]) {
-  dma_kstep<0, IIB>(c, kt, acc, f0a, f0b, f1a, f1b);
-  dma_kstep<1, IIB>(c, kt, acc, f1a, f1b, f0a, f0b);
+template <int IIB, int WGM, int WGN>
+__device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
+                                          f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
+                                          u32x4_t (&f0a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f0b)[dma::Grid<WGM, WGN>::FN],
+                                          u32x4_t (&f1a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f1b)[dma::Grid<WGM, WGN>::FN]) {
+  dma_kstep<0, IIB, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
+  dma_kstep<1, IIB, WGM, WGN>(c, kt, acc, f1a, f1b, f0a, f0b);
   if constexpr (dma::KK == 4) {
-    dma_kstep<2, IIB>(c, kt, acc, f0a, f0b, f1a, f1b);
-    dma_kstep<3, IIB>(c, kt, acc, f1a, f1b, f0a, f0b);
+    dma_kstep<2, IIB, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
+    dma_kstep<3, IIB, WGM, WGN>(c, kt, acc, f1a, f1b, f0a, f0b);
   }
 }
 
@@ -618,9 +642,11 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt, f32x16_t (&ac
 // is added inside the main loop by scaled-identity MFMAs against the Q
 // fragments, so the epilogue reads nothing back from global memory. AXPY
 // always folds.
-template <int EPI, bool FOLD>
+template <int EPI, bool FOLD, int WGM, int WGN>
 __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem) {
   using namespace dma;
+  using Gd = Grid<WGM, WGN>;
+  constexpr int FM = Gd::FM, FN = Gd::FN, DPW = Gd::DPW, NW = Gd::NW;
   const NsGroup& G = args.g[J.gi];
   // an opaque copy of the thread index: without it the compiler hoists every
   // lane-dependent address of the tile out of a persistent block's job loop
@@ -631,31 +657,32 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int tid = (wave << 6) | lane;
 
-  // DMA source of this wave: waves 0,1 load P rows [w*128, +128), waves 2,3
-  // Q rows [(w-2)*128, +128); P and Q rows are contiguous in the stage.
+  // DMA source of this wave: the first NW/2 waves load P rows
+  // [w*PANEL, +PANEL), the others the matching rows of Q; P and Q rows are
+  // contiguous in the stage.
   DmaCtx c;
   c.smem = smem;
-  c.wave_fill = smem + wave * (DMA_PER_WAVE * 1024);
+  c.wave_fill = smem + wave * (DPW * 1024);
   c.lane = lane;
-  c.wm = wave >> 1;
-  c.wn = wave & 1;
+  c.wm = wave / WGN;
+  c.wn = wave % WGN;
   c.nk = G.K / BK;   // K is a multiple of 256: nk >= 4
   c.a = EPI == EPI_POLY ? args.b / args.c : args.a;
-  const bool isP = wave < 2;
+  const bool isP = wave < NW / 2;
   c.ld_src = isP ? G.ldP : G.ldQ;
   c.src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
-          (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave & 1) * 128) * c.ld_src;
+          (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave % (NW / 2)) * Gd::PANEL) * c.ld_src;
   // instruction q adds q*RPI rows; swz of the stage row depends on q only
-  // through q & 1 (panels start at multiples of 128 rows)
+  // through q & 1 (panels start at multiples of 64 rows)
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     c.lane_off[par] = (lane / CPR) * c.ld_src + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -665,31 +692,31 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   // run.
 #pragma unroll
   for (int t = 0; t < STAGES; ++t)
-    dma_issue(c.wave_fill + t * STAGE_BYTES, c.src, c.ld_src, c.lane_off, t * BK);
-  dma_wait_tiles(STAGES - 1);   // this wave's part of tile 0 has landed
+    dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.ld_src, c.lane_off, t * BK);
+  dma_wait_tiles<DPW>(STAGES - 1);   // this wave's part of tile 0 has landed
   __builtin_amdgcn_s_barrier();
-  u32x4_t f0a[4], f0b[4], f1a[4], f1b[4];
-  dma_read_step(smem, 0, lane, c.wm, c.wn, f0a, f0b);
+  u32x4_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
+  dma_read_step<WGM, WGN>(smem, 0, lane, c.wm, c.wn, f0a, f0b);
   int kt = 0;
   if constexpr (FOLD) {
     // the k-tiles whose k range is this wave's 128 output rows (K = m_pad,
     // so they lie inside [0, nk)) carry the a*X (AXPY) or (b/c)*A (POLY)
     // term: Q rows j hold X^T[j][k] = X[k][j], or A[j][k] = A[k][j]
-    const int e_first = (J.bi * BM + c.wm * 128) / BK;
-    for (; kt < e_first; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
+    const int e_first = (J.bi * BM + c.wm * Gd::WTM) / BK;
+    for (; kt < e_first; ++kt) dma_ktile<-1, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
     if constexpr (BK == 32) {
-      dma_ktile<0>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<1>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<2>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<3>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<0, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<1, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<2, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<3, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
     } else {
-      dma_ktile<0>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<2>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<0, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<2, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
     }
   }
-  for (; kt < c.nk; ++kt) dma_ktile<-1>(c, kt, acc, f0a, f0b, f1a, f1b);
+  for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, 2, 2, FOLD>(args, G, J, acc, smem, tid);
+  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD>(args, G, J, acc, smem, tid);
 }
 
 // Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
@@ -698,8 +725,8 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
 // the longest jobs first and, where jobs differ in K, a fixed stride ends
 // about as late as taking jobs on demand would (the blocks holding one long
 // and two short jobs set the end either way).
-template <int EPI, bool FOLD>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int EPI, bool FOLD, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 ns_gemm_dma(const NsArgs args) {
   using namespace dma;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES];
@@ -707,7 +734,7 @@ ns_gemm_dma(const NsArgs args) {
   const int P = (int)(gridDim.x >> 3);
   TileJob J;
   for (int local = (int)(blockIdx.x >> 3); map_job_at(args, x, local, J); local += P) {
-    dma_tile<EPI, FOLD>(args, J, smem);
+    dma_tile<EPI, FOLD, WGM, WGN>(args, J, smem);
     __syncthreads();   // the epilogue is done with LDS before the next job's DMA
   }
 }
@@ -732,10 +759,21 @@ static hipError_t launch_reg_epi(int epi, const NsArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int EPI, bool FOLD>
+template <int EPI, bool FOLD, int WGM, int WGN>
 static hipError_t launch_dma(const NsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD>), dim3(a.padded_blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD, WGM, WGN>), dim3(a.padded_blocks), dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
+}
+
+template <int WGM, int WGN>
+static hipError_t launch_dma_epi(int epi, const NsArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_GRAM: return launch_dma<EPI_GRAM, false, WGM, WGN>(a, s);
+    case EPI_POLY:
+      return a.c != 0.0f ? launch_dma<EPI_POLY, true, WGM, WGN>(a, s) : launch_dma<EPI_POLY, false, WGM, WGN>(a, s);
+    case EPI_AXPY: return launch_dma<EPI_AXPY, true, WGM, WGN>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 #define MA_NS_TILE(BM_, BN_, BK_, WGM_, WGN_)                                                      \
@@ -749,12 +787,8 @@ hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipS
   if (dtype == DT_BF16) {
     if (tile.dma) {
       if (tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK) return hipErrorInvalidValue;
-      switch (epi) {
-        case EPI_GRAM: return launch_dma<EPI_GRAM, false>(a, s);
-        case EPI_POLY:
-          return a.c != 0.0f ? launch_dma<EPI_POLY, true>(a, s) : launch_dma<EPI_POLY, false>(a, s);
-        case EPI_AXPY: return launch_dma<EPI_AXPY, true>(a, s);
-      }
+      if (tile.wgm == 2 && tile.wgn == 2) return launch_dma_epi<2, 2>(epi, a, s);
+      if (tile.wgm == 2 && tile.wgn == 4) return launch_dma_epi<2, 4>(epi, a, s);
       return hipErrorInvalidValue;
     }
     constexpr int DTv = DT_BF16;
