@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (one captured step replayed --steps times)")
     ap.add_argument("--no-lion", action="store_true", help="skip the separate Lion step timing")
+    ap.add_argument("--no-practical", action="store_true", help="skip the practical-peak calibration kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed steps, run 3 plain device copies of MIB MiB (read MIB, write MIB) "
                          "as the known-size reference that scales HBM byte counters")
@@ -219,7 +220,7 @@ def main():
                     "traffic": traffic_for(dom, wl.name)}
 
     lion = None if args.no_lion else lion_timing(M, wl, dev, args.steps)
-    practical = practical_peaks(L, lib, dev)
+    practical = None if args.no_practical else practical_peaks(L, lib, dev)
     if roofline is not None and practical:
         key = "mfma_bf16" if roofline["bound"] == "mfma" else "copy"
         if roofline["unit"] == practical[key]["unit"] and roofline.get("achieved"):
