@@ -13,15 +13,17 @@
 // stores, staged through LDS so that global stores are 16-byte coalesced.
 //
 // Two kernels share the job mapping and the epilogue:
-//  * ns_gemm_dma (bf16): 256 x 256 block tile, 4 waves of 128 x 128 (32x32x16
-//    MFMAs, 16 accumulator blocks per wave). Operand tiles of 256 x 64 move
-//    from global memory straight into a 2-stage LDS ring with
-//    global_load_lds_dwordx4 (no VGPR staging), one tile ahead of the one
-//    being multiplied; 16-byte chunks are XOR-swizzled by row so that the
-//    fragment reads are conflict-free. Blocks are persistent, one per CU,
-//    each walking a fixed share of its XCD's tile list.
-//  * ns_gemm_reg (fp32, and bf16 for small matrices): a register-staged
-//    double-buffered kernel of configurable tile and wave layout.
+//  * ns_gemm_dma (bf16): 256 x 256 block tile, 8 waves of 128 x 64, two per
+//    SIMD (32x32x16 MFMAs, 8 accumulator blocks per wave; a 4-wave form of
+//    128 x 128 is built too). Operand tiles of 256 x 64 move from global
+//    memory straight into a 2-stage LDS ring with global_load_lds_dwordx4 (no
+//    VGPR staging), one tile ahead of the one being multiplied; 16-byte chunks
+//    are XOR-swizzled by row so that the fragment reads are conflict-free.
+//    Blocks are persistent, one per CU, each walking a fixed share of its
+//    XCD's tile list.
+//  * ns_gemm_reg (fp32; bf16 only through the tile override of the host
+//    plan): a register-staged double-buffered kernel of configurable tile and
+//    wave layout.
 // Blocks are dealt to the 8 XCDs so that each XCD gets an eighth of every
 // shape group, whole matrices at a time where possible (see NsArgs).
 #include "ns_gemm.hpp"
