@@ -61,12 +61,20 @@ def work_model(wl, ns_steps):
     ex = elem_bytes(wl.ns_precision)
     ep, eg, em = elem_bytes(wl.param_dtype), elem_bytes(wl.grad_dtype), elem_bytes(wl.mom_dtype)
     gram = poly = axpy = 0.0
+    gram_b = poly_b = axpy_b = 0.0
     pre = rown = post = 0.0
+    T = max(ns_steps, 1)
     for g in wl.muon_groups:
         m, n = min(g.rows, g.cols), max(g.rows, g.cols)
         gram += g.count * m * m * n          # A = X X^T, symmetric: m^2 n
         poly += g.count * m * m * m          # A A, symmetric: m^3
         axpy += g.count * 2.0 * m * m * n    # B X: 2 m^2 n
+        # operands read once, outputs written once: GRAM reads X, writes A;
+        # POLY reads A, writes B; AXPY reads B and X^T and writes X' and X'^T
+        # (the last of the T launches writes one layout: mean per launch)
+        gram_b += g.count * (m * n + m * m) * ex
+        poly_b += g.count * (2.0 * m * m) * ex
+        axpy_b += g.count * (m * m + m * n + m * n * (2.0 * T - 1.0) / T) * ex
         e = g.rows * g.cols * g.count
         rown += e * (eg + em)                # read G, M
         pre += e * (eg + 2 * em + 2 * ex)    # read G, M; write M, X0, X0^T
@@ -74,6 +82,7 @@ def work_model(wl, ns_steps):
     adam = 28.0 * wl.adamw_numel
     return {
         "gram": ("TFLOP/s", gram), "poly": ("TFLOP/s", poly), "axpy": ("TFLOP/s", axpy),
+        "gemm_bytes": {"gram": gram_b, "poly": poly_b, "axpy": axpy_b},
         "rownorm": ("GB/s", rown), "pre": ("GB/s", pre), "post": ("GB/s", post), "adamw": ("GB/s", adam),
         "ns_total_flops_per_step": ns_steps * (gram + poly + axpy),
     }
@@ -203,6 +212,10 @@ def main():
                 per_launch = work * (args.steps / n.value) if unit == "GB/s" else work
                 if unit == "TFLOP/s":
                     rec.update(achieved=round(per_launch / (avg_ms * 1e-3) / 1e12, 2), unit=unit)
+                    b = model["gemm_bytes"][name]
+                    rec.update(achieved_hbm=round(b / (avg_ms * 1e-3) / 1e9, 1),
+                               algorithmic_bytes_per_launch=round(b),
+                               algorithmic_flops_per_launch=round(per_launch))
                 else:
                     rec.update(achieved=round(per_launch / (avg_ms * 1e-3) / 1e9, 1), unit=unit)
             kernels[name] = rec
@@ -213,11 +226,25 @@ def main():
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
         r = kernels[dom]
-        bound = "mfma" if r.get("unit") == "TFLOP/s" else "hbm"
+        if r.get("unit") == "TFLOP/s":
+            # the binding roofline of a GEMM: its flops at the MFMA peak or its
+            # algorithmic bytes at the HBM peak, whichever takes longer
+            t_f = model[dom][1] / (peak_f * 1e12)
+            t_b = model["gemm_bytes"][dom] / (PEAK_HBM_GBS * 1e9)
+            bound = "mfma" if t_f >= t_b else "hbm"
+        else:
+            bound = "hbm"
+        if bound == "mfma" or r.get("unit") != "TFLOP/s":
+            achieved, unit = r.get("achieved"), r.get("unit")
+        else:
+            achieved, unit = r.get("achieved_hbm"), "GB/s"
         peak = peak_f if bound == "mfma" else PEAK_HBM_GBS
-        roofline = {"kernel": dom, "bound": bound, "achieved": r.get("achieved"), "peak": peak,
-                    "unit": r.get("unit"), "frac": round(r.get("achieved", 0) / peak, 4),
+        roofline = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                    "unit": unit, "frac": round((achieved or 0) / peak, 4),
                     "traffic": traffic_for(dom, wl.name)}
+        if r.get("unit") == "TFLOP/s":
+            roofline.update(mfma_frac=round(r["achieved"] / peak_f, 4),
+                            hbm_frac=round(r["achieved_hbm"] / PEAK_HBM_GBS, 4))
 
     lion = None if args.no_lion else lion_timing(M, wl, dev, args.steps)
     practical = None if args.no_practical else practical_peaks(L, lib, dev)
