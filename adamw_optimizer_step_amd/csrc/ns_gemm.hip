@@ -95,8 +95,18 @@ __device__ __forceinline__ bool map_job_at(const NsArgs& args, int x, int local,
         while (t >= len) { t -= len; ++bi; --len; }
         bj = bi + t;
       } else {
-        bi = t / G.tn;
-        bj = t - bi * G.tn;
+        // bands of up to 4 tile rows, walked column by column: the blocks of
+        // an XCD working at the same time cover a 4 x 8 patch of tiles, whose
+        // 12 operand panels are read in step along K and shared in L2 (a row
+        // of 32 tiles would stream 32 distinct panels of Q). The symmetric
+        // products gained nothing from the same order.
+        constexpr int kBand = 4;
+        const int band = t / (kBand * G.tn);
+        const int rem = G.tm - band * kBand;
+        const int bh = rem < kBand ? rem : kBand;
+        const int idx = t - band * kBand * G.tn;
+        bj = idx / bh;
+        bi = band * kBand + (idx - bj * bh);
       }
       J.gi = q;
       J.mat = mat;
