@@ -79,6 +79,18 @@ NsTile parse_tile(const char* env, NsTile d) {
   return d;
 }
 
+NsTile ns_tile(int dtype, bool symmetric);
+
+// Whether the AXPY launches read X^T from the row-major X through transposing
+// LDS reads (NsTile::qt): the 8-wave bf16 LDS-DMA tile, unless MA_NS_QT=0.
+// Then no X^T copy of the iterate is written.
+bool ns_q_transposed(int dtype) {
+  if (dtype != MA_BF16) return false;
+  static const bool off = [] { const char* e = getenv("MA_NS_QT"); return e && strcmp(e, "0") == 0; }();
+  const NsTile t = ns_tile(dtype, false);
+  return !off && t.dma && t.wgm == 2 && t.wgn == 4 && t.bk == 64;
+}
+
 NsTile ns_tile(int dtype, bool symmetric) {
   if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
   // the LDS-DMA kernel with 8 waves (2 x 4 of 128 x 64, two per SIMD); "dma"
@@ -286,7 +298,9 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
     const int cur = step & 1, nxt = cur ^ 1;
     const bool last = step == T - 1;
     for (int epi = EPI_GRAM; epi <= EPI_AXPY; ++epi) {
-      const NsTile tile = ns_tile(dtype, epi != EPI_AXPY);
+      NsTile tile = ns_tile(dtype, epi != EPI_AXPY);
+      const bool qt = epi == EPI_AXPY && ns_q_transposed(dtype);
+      tile.qt = qt ? 1 : 0;
       if (epi != EPI_AXPY && tile.bm != tile.bn) return fail(MA_ERR_INVALID_ARG, "symmetric GEMM tile must be square");
       for (size_t base = 0; base < order.size(); base += kMaxNsGroups) {
         NsArgs A{};
@@ -321,16 +335,18 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.P = ws + p.off_b;
             G.sP = p.a_stride;
             G.ldP = (int32_t)p.m_pad;
-            G.Q = ws + p.off_xt[cur];
+            // Q = X^T: its own copy, or (qt) X itself read transposed
+            G.Q = ws + (qt ? p.off_x[cur] : p.off_xt[cur]);
             G.sQ = p.x_stride;
-            G.ldQ = (int32_t)p.m_pad;
+            G.ldQ = (int32_t)(qt ? p.n_pad : p.m_pad);
             G.K = (int32_t)p.m_pad;
-            G.E = ws + p.off_xt[cur];
+            G.E = ws + p.off_xt[cur];   // not read: AXPY folds a*X into its main loop
             G.sE = p.x_stride;
             G.ldE = (int32_t)p.m_pad;
-            // the last step writes only the copy in the parameter's layout
+            // the last step writes only the copy in the parameter's layout;
+            // the others X' and, unless qt, X'^T
             G.outN = (!last || !p.tall) ? (void*)(ws + p.off_x[nxt]) : nullptr;
-            G.outT = (!last || p.tall) ? (void*)(ws + p.off_xt[nxt]) : nullptr;
+            G.outT = ((!last && !qt) || (last && p.tall)) ? (void*)(ws + p.off_xt[nxt]) : nullptr;
             G.sN = G.sT = p.x_stride;
             G.ldN = (int32_t)p.n_pad;
             G.ldT = (int32_t)p.m_pad;
@@ -481,7 +497,15 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
       if (err != hipSuccess) return hip_fail(err, "row norms");
       { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
       if (err != hipSuccess) return hip_fail(err, "norm finalize");
-      { ProfScope ps(MA_K_PRE, s); err = launch_pre(p.dt_g, p.dt_m, p.dt_x, a, s); }
+      ElemArgs ap = a;
+      if (ns_q_transposed(p.dt_x)) {
+        // X0 in the iteration's layout X (for T > 0) and in the parameter's
+        // layout (for T = 0); X0^T is not needed
+        const bool t0 = hp->ns_steps == 0;
+        if (!t0 && p.tall) ap.xd = nullptr;   // parameter's layout is X^T
+        if (t0 || !p.tall) ap.xt = nullptr;   // the transposed view is X^T
+      }
+      { ProfScope ps(MA_K_PRE, s); err = launch_pre(p.dt_g, p.dt_m, p.dt_x, ap, s); }
       if (err != hipSuccess) return hip_fail(err, "momentum/X0");
     }
   }

@@ -176,7 +176,8 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
   const int tid = threadIdx.x;
   const int cl = (tid & 7) * 8;
   const bool vec = a.vec != 0;
-  void* xd = eptr<DTX>(a.xd, (int64_t)k * a.x_stride);
+  // either copy may be skipped (null): the iteration may need only one layout
+  void* xd = a.xd ? eptr<DTX>(a.xd, (int64_t)k * a.x_stride) : nullptr;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int rl = (tid >> 3) + 32 * h;
@@ -216,7 +217,7 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.0f;
     }
-    if (r < a.r_ext) {
+    if (xd && r < a.r_ext) {
       const int64_t off = (int64_t)r * a.ld_d + c;
       if (c + 8 <= a.c_ext && (a.ld_d & 7) == 0) {
         store8<DTX>(eptr<DTX>(xd, off), x);

@@ -3,14 +3,18 @@
 // One quintic Newton-Schulz step X <- a X + (b A + c A A) X, A = X X^T, is
 // three products ("Chapter 4: The MuonAdamW Optimizer", section "Polar
 // Express: Newton-Schulz Orthogonalization"; "3.9 Optimizers ...", section
-// "Muon: Orthogonalizing the Update"). Every iterate X (m x n, m <= n) is kept
-// in two layouts, X and X^T, so that all three are of one form,
-//     C[i][j] = sum_k P[i][k] * Q[j][k]        (both operands K-contiguous):
+// "Muon: Orthogonalizing the Update"). All three are of one form,
+//     C[i][j] = sum_k P[i][k] * Q[j][k]:
 //   GRAM  A  = X X^T        P = Q = X       K = n   A symmetric: tiles bi <= bj
 //   POLY  B  = b A + c A A  P = Q = A       K = m   A A = A A^T; B symmetric
-//   AXPY  X' = a X + B X    P = B, Q = X^T  K = m   writes X' and X'^T
-// The epilogues fuse the a/b/c combination and the mirrored or dual-layout
-// stores, staged through LDS so that global stores are 16-byte coalesced.
+//   AXPY  X' = a X + B X    P = B, Q = X^T  K = m
+// with the iterate X (m x n, m <= n) row-major. P and Q are read as
+// K-contiguous rows, except AXPY's Q in the 8-wave bf16 kernel: its k-tiles
+// are rows of X, and the fragments come from transposing LDS reads, so X^T is
+// never stored (AXPY writes X' only). The fp32 kernel reads an X^T copy,
+// which its AXPY writes beside X'. The epilogues fuse the a/b/c combination
+// and the mirrored or dual-layout stores, staged through LDS so that global
+// stores are 16-byte coalesced.
 //
 // Two kernels share the job mapping and the epilogue:
 //  * ns_gemm_dma (bf16): 256 x 256 block tile, 8 waves of 128 x 64, two per
@@ -488,7 +492,7 @@ __device__ __forceinline__ void dma_wait_tiles(int tiles) {
 // Fragment reads of MFMA k-step kk (16 values of k) of a k-tile: this wave's
 // FM 32-row blocks of P (fa) and FN of Q (fb); lane (l32, lh) reads row l32
 // of each block at logical chunk 2 kk + lh.
-template <int WGM, int WGN>
+template <int WGM, int WGN, bool QT = false>
 __device__ __forceinline__ void dma_read_step(const unsigned char* cur, int kk, int lane, int wm, int wn,
                                               u32x4_t (&fa)[dma::Grid<WGM, WGN>::FM],
                                               u32x4_t (&fb)[dma::Grid<WGM, WGN>::FN]) {
@@ -500,11 +504,46 @@ __device__ __forceinline__ void dma_read_step(const unsigned char* cur, int kk, 
     const int r = wm * Gd::WTM + i * 32 + l32;
     fa[i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
   }
+  if constexpr (!QT) {
 #pragma unroll
-  for (int j = 0; j < Gd::FN; ++j) {
-    const int r = BM + wn * Gd::WTN + j * 32 + l32;
-    fb[j] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
+    for (int j = 0; j < Gd::FN; ++j) {
+      const int r = BM + wn * Gd::WTN + j * 32 + l32;
+      fb[j] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
+    }
   }
+}
+
+// Q read transposed (QT): the Q half of a stage holds 64 rows k of Q^T (row
+// pitch 512 bytes: 256 values j), 16-byte chunk c of row k stored at chunk
+// c ^ (4 (k % 4)). ds_read_b64_tr_b16 works on groups of 16 lanes: lane
+// 4a + b of a group addresses 4 values (a row, 4 consecutive columns) and
+// receives value b' of the addresses of lanes 4e + a' (e = 0..3), where
+// 4a' + b' is its own index in the group. With lane 4a + b addressing row
+// r0 + a, columns c0 + 4b .. +3, lane 4a' + b' receives column c0 + 4a' + b'
+// of rows r0 .. r0 + 3. Two such reads per 32 columns give lane (l32, lh)
+// the values k = 16 kk + 8 lh + 0..7 of column l32, in the slot order of the
+// P fragments. qoff[j] (per lane, bytes from the Q half) addresses row
+// 8 (g / 2) + a, columns 32 j' + 16 (g % 2) + 4 b of block j, g = lane / 16;
+// the row offsets 16 kk and 16 kk + 4 are immediates. The reads wait for
+// their results inside the statement.
+constexpr int QT_HALF = dma::BM * dma::ROWB;   // byte offset of the Q half in a stage
+template <int KK>
+__device__ __forceinline__ void qtr_read(const unsigned char* stage, const uint32_t (&qoff)[2], u32x4_t (&fb)[2]) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) const unsigned char lds_cu8_t;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_cu8_t*)stage + QT_HALF;
+  u32x2_t r00, r01, r10, r11;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r00), "=&v"(r01), "=&v"(r10), "=&v"(r11)
+      : "v"(base + qoff[0]), "v"(base + qoff[1]), "i"(KK * 16 * 512), "i"((KK * 16 + 4) * 512)
+      : "memory");
+  fb[0] = u32x4_t{r00.x, r00.y, r01.x, r01.y};
+  fb[1] = u32x4_t{r10.x, r10.y, r11.x, r11.y};
 }
 
 // This wave's DMA of one k-tile (its panel of the stage: PANEL rows of P or
@@ -512,22 +551,22 @@ __device__ __forceinline__ void dma_read_step(const unsigned char* cur, int kk, 
 // q*RPI .. q*RPI+RPI-1 of the wave's panel; lane i lands at byte 1024 q + 16 i
 // (row q*RPI + i/CPR, physical chunk i%CPR) and so loads logical chunk
 // (i%CPR) ^ swz(row) from memory: lane_off[q & 1] holds that offset.
+// q_step: elements between the sources of consecutive instructions (RPI
+// rows); koff: the k-tile's offset in elements. With Q read transposed, a Q
+// wave's instruction covers 2 rows of 512 bytes instead (q_step = 2 rows,
+// koff = k0 rows).
 template <int DPW>
-__device__ __forceinline__ void dma_issue(unsigned char* fill, const uint16_t* src, int ld_src,
-                                          const int (&lane_off)[2], int k0) {
-  using namespace dma;
+__device__ __forceinline__ void dma_issue(unsigned char* fill, const uint16_t* src, int64_t q_step,
+                                          const int (&lane_off)[2], int64_t koff) {
 #pragma unroll
   for (int q = 0; q < DPW; ++q)
-    __builtin_amdgcn_global_load_lds(src + (int64_t)(q * RPI) * ld_src + lane_off[q & 1] + k0,
-                                     (lds_void_t*)(fill + q * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + q * q_step + lane_off[q & 1] + koff, (lds_void_t*)(fill + q * 1024), 16, 0, 0);
 }
 
 // One DMA instruction q of this wave's share of a k-tile (see dma_issue)
-__device__ __forceinline__ void dma_issue_one(unsigned char* fill, const uint16_t* src, int ld_src,
-                                              const int (&lane_off)[2], int k0, int q) {
-  using namespace dma;
-  __builtin_amdgcn_global_load_lds(src + (int64_t)(q * RPI) * ld_src + lane_off[q & 1] + k0,
-                                   (lds_void_t*)(fill + q * 1024), 16, 0, 0);
+__device__ __forceinline__ void dma_issue_one(unsigned char* fill, const uint16_t* src, int64_t q_step,
+                                              const int (&lane_off)[2], int64_t koff, int q) {
+  __builtin_amdgcn_global_load_lds(src + q * q_step + lane_off[q & 1] + koff, (lds_void_t*)(fill + q * 1024), 16, 0, 0);
 }
 
 // MFMAs of one k-step for accumulator rows [I0, I1)
@@ -568,8 +607,10 @@ struct DmaCtx {
   unsigned char* smem;
   unsigned char* wave_fill;
   const uint16_t* src;
+  int64_t q_step, k_step;   // DMA source step per instruction and per k-tile (elements)
   int ld_src, lane, wm, wn, nk;
   int lane_off[2];
+  uint32_t qoff[2];         // transposed Q fragment addresses (QT)
   float a;
 };
 
@@ -582,7 +623,7 @@ struct DmaCtx {
 // Q = X^T) or A[i][j] (POLY, A symmetric) for them, so (a I) Q-block adds
 // a*X, or (b/c)*A, to the accumulators instead of reading it back in the
 // epilogue.
-template <int KKI, int IIB, int WGM, int WGN>
+template <int KKI, int IIB, int WGM, int WGN, bool QT>
 __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
                                           f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
                                           u32x4_t (&fa)[dma::Grid<WGM, WGN>::FM], u32x4_t (&fb)[dma::Grid<WGM, WGN>::FN],
@@ -596,7 +637,7 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
     // (read during the previous k-step) is not also a wait for the new reads
     mfma_rows<0, 1>(acc, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
-    dma_read_step<WGM, WGN>(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
+    dma_read_step<WGM, WGN, QT>(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
     __builtin_amdgcn_sched_barrier(0);
     mfma_rows<1, FM>(acc, fa, fb);
   } else {
@@ -611,7 +652,7 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
       const int later = c.nk - 2 - kt;
       dma_wait_tiles<DPW>(later < STAGES - 2 ? later : STAGES - 2);
       __builtin_amdgcn_s_barrier();
-      dma_read_step<WGM, WGN>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
+      dma_read_step<WGM, WGN, QT>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
     }
     __builtin_amdgcn_sched_barrier(0);
     // the DMA of tile kt+STAGES into the stage just released, one instruction
@@ -619,32 +660,41 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
     // at the CU's one texture-address unit and hold up the MFMAs behind them
     const bool fill = kt + STAGES < c.nk;
     unsigned char* fill_at = c.wave_fill + s_cur * STAGE_BYTES;
-    const int k0 = (kt + STAGES) * BK;
+    const int64_t koff = (int64_t)(kt + STAGES) * c.k_step;
 #pragma unroll
     for (int idx = 0; idx < FM * FN; ++idx) {
       mfma_frag<DT_BF16>(acc[idx / FN][idx % FN], fa[idx / FN], fb[idx % FN]);
 #pragma unroll
       for (int q = idx * DPW / (FM * FN); q < (idx + 1) * DPW / (FM * FN); ++q)
-        if (fill) dma_issue_one(fill_at, c.src, c.ld_src, c.lane_off, k0, q);
+        if (fill) dma_issue_one(fill_at, c.src, c.q_step, c.lane_off, koff, q);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (IIB >= 0) ident_step<IIB + KKI / 2>(acc, fb, KKI % 2, c.lane, c.a);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (QT) {
+    // the next k-step's Q fragments, after this k-step's MFMAs are queued
+    if constexpr (KKI + 1 < KK) {
+      qtr_read<KKI + 1>(c.smem + s_cur * STAGE_BYTES, c.qoff, nb);
+    } else {
+      if (kt + 1 < c.nk) qtr_read<0>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, c.qoff, nb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // One k-tile: KK k-steps, the fragment sets alternating (0, 1) -> (1, 0) -> ...
 // so that (f0a, f0b) again hold the next tile's first k-step afterwards.
-template <int IIB, int WGM, int WGN>
+template <int IIB, int WGM, int WGN, bool QT>
 __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
                                           f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
                                           u32x4_t (&f0a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f0b)[dma::Grid<WGM, WGN>::FN],
                                           u32x4_t (&f1a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f1b)[dma::Grid<WGM, WGN>::FN]) {
-  dma_kstep<0, IIB, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
-  dma_kstep<1, IIB, WGM, WGN>(c, kt, acc, f1a, f1b, f0a, f0b);
+  dma_kstep<0, IIB, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
+  dma_kstep<1, IIB, WGM, WGN, QT>(c, kt, acc, f1a, f1b, f0a, f0b);
   if constexpr (dma::KK == 4) {
-    dma_kstep<2, IIB, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
-    dma_kstep<3, IIB, WGM, WGN>(c, kt, acc, f1a, f1b, f0a, f0b);
+    dma_kstep<2, IIB, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
+    dma_kstep<3, IIB, WGM, WGN, QT>(c, kt, acc, f1a, f1b, f0a, f0b);
   }
 }
 
@@ -654,7 +704,7 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
 // is added inside the main loop by scaled-identity MFMAs against the Q
 // fragments, so the epilogue reads nothing back from global memory. AXPY
 // always folds.
-template <int EPI, bool FOLD, int WGM, int WGN>
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT>
 __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem) {
   using namespace dma;
   using Gd = Grid<WGM, WGN>;
@@ -682,13 +732,39 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   c.a = EPI == EPI_POLY ? args.b / args.c : args.a;
   const bool isP = wave < NW / 2;
   c.ld_src = isP ? G.ldP : G.ldQ;
-  c.src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
-          (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave % (NW / 2)) * Gd::PANEL) * c.ld_src;
-  // instruction q adds q*RPI rows; swz of the stage row depends on q only
-  // through q & 1 (panels start at multiples of 64 rows)
+  if (QT && !isP) {
+    // Q read transposed: Q^T row-major ([k][j], pitch ldQ); this wave loads
+    // rows k0 + 16 w .. +15 (w = wave - NW/2), columns bj*BN .. +BN, two
+    // 512-byte rows per instruction; lane i lands at row i / 32, physical
+    // chunk i % 32, so it loads logical chunk (i % 32) ^ (4 (row % 4))
+    static_assert(!QT || (NW == 8 && Gd::FN == 2 && BN == 256 && BK == 64 && STAGES == 2), "QT layout");
+    c.src = reinterpret_cast<const uint16_t*>(G.Q) + (int64_t)J.mat * G.sQ +
+            (int64_t)((wave - NW / 2) * 16) * c.ld_src + (int64_t)J.bj * BN;
+    c.q_step = 2 * (int64_t)c.ld_src;
+    c.k_step = (int64_t)BK * c.ld_src;
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    c.lane_off[par] = (lane / CPR) * c.ld_src + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
+    for (int par = 0; par < 2; ++par)
+      c.lane_off[par] = (lane >> 5) * c.ld_src + (((lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3))) << 3);
+  } else {
+    c.src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
+            (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave % (NW / 2)) * Gd::PANEL) * c.ld_src;
+    c.q_step = (int64_t)RPI * c.ld_src;
+    c.k_step = BK;
+    // instruction q adds q*RPI rows; swz of the stage row depends on q only
+    // through q & 1 (panels start at multiples of 64 rows)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      c.lane_off[par] = (lane / CPR) * c.ld_src + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
+  }
+  if constexpr (QT) {
+    // transposed Q fragment addresses (see qtr_read)
+    const int g = lane >> 4, a4 = (lane >> 2) & 3, b4 = lane & 3;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int chunk = (c.wn * Gd::WTN + j * 32) / 8 + 2 * (g & 1) + (b4 >> 1);
+      c.qoff[j] = (uint32_t)((8 * (g >> 1) + a4) * 512 + ((chunk ^ (4 * a4)) << 4) + (b4 & 1) * 8);
+    }
+  }
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -704,29 +780,30 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   // run.
 #pragma unroll
   for (int t = 0; t < STAGES; ++t)
-    dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.ld_src, c.lane_off, t * BK);
+    dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.q_step, c.lane_off, (int64_t)t * c.k_step);
   dma_wait_tiles<DPW>(STAGES - 1);   // this wave's part of tile 0 has landed
   __builtin_amdgcn_s_barrier();
   u32x4_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
-  dma_read_step<WGM, WGN>(smem, 0, lane, c.wm, c.wn, f0a, f0b);
+  dma_read_step<WGM, WGN, QT>(smem, 0, lane, c.wm, c.wn, f0a, f0b);
+  if constexpr (QT) qtr_read<0>(smem, c.qoff, f0b);
   int kt = 0;
   if constexpr (FOLD) {
     // the k-tiles whose k range is this wave's 128 output rows (K = m_pad,
     // so they lie inside [0, nk)) carry the a*X (AXPY) or (b/c)*A (POLY)
     // term: Q rows j hold X^T[j][k] = X[k][j], or A[j][k] = A[k][j]
     const int e_first = (J.bi * BM + c.wm * Gd::WTM) / BK;
-    for (; kt < e_first; ++kt) dma_ktile<-1, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
+    for (; kt < e_first; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
     if constexpr (BK == 32) {
-      dma_ktile<0, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<1, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<2, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<3, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<0, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<1, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<2, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<3, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
     } else {
-      dma_ktile<0, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<2, WGM, WGN>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<0, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
+      dma_ktile<2, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
     }
   }
-  for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN>(c, kt, acc, f0a, f0b, f1a, f1b);
+  for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
   ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD>(args, G, J, acc, smem, tid);
 }
@@ -737,7 +814,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
 // the longest jobs first and, where jobs differ in K, a fixed stride ends
 // about as late as taking jobs on demand would (the blocks holding one long
 // and two short jobs set the end either way).
-template <int EPI, bool FOLD, int WGM, int WGN>
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT>
 __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 ns_gemm_dma(const NsArgs args) {
   using namespace dma;
@@ -746,7 +823,7 @@ ns_gemm_dma(const NsArgs args) {
   const int P = (int)(gridDim.x >> 3);
   TileJob J;
   for (int local = (int)(blockIdx.x >> 3); map_job_at(args, x, local, J); local += P) {
-    dma_tile<EPI, FOLD, WGM, WGN>(args, J, smem);
+    dma_tile<EPI, FOLD, WGM, WGN, QT>(args, J, smem);
     __syncthreads();   // the epilogue is done with LDS before the next job's DMA
   }
 }
@@ -771,14 +848,21 @@ static hipError_t launch_reg_epi(int epi, const NsArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int EPI, bool FOLD, int WGM, int WGN>
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT = false>
 static hipError_t launch_dma(const NsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD, WGM, WGN>), dim3(a.padded_blocks), dim3(64 * WGM * WGN), 0, s, a);
+  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD, WGM, WGN, QT>), dim3(a.padded_blocks), dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
 
 template <int WGM, int WGN>
-static hipError_t launch_dma_epi(int epi, const NsArgs& a, hipStream_t s) {
+static hipError_t launch_dma_epi(int epi, bool qt, const NsArgs& a, hipStream_t s) {
+  if (qt) {
+    // AXPY with Q read transposed (8-wave form only)
+    if constexpr (WGM == 2 && WGN == 4) {
+      if (epi == EPI_AXPY) return launch_dma<EPI_AXPY, true, WGM, WGN, true>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case EPI_GRAM: return launch_dma<EPI_GRAM, false, WGM, WGN>(a, s);
     case EPI_POLY:
@@ -799,8 +883,8 @@ hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipS
   if (dtype == DT_BF16) {
     if (tile.dma) {
       if (tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK) return hipErrorInvalidValue;
-      if (tile.wgm == 2 && tile.wgn == 2) return launch_dma_epi<2, 2>(epi, a, s);
-      if (tile.wgm == 2 && tile.wgn == 4) return launch_dma_epi<2, 4>(epi, a, s);
+      if (tile.wgm == 2 && tile.wgn == 2) return launch_dma_epi<2, 2>(epi, tile.qt != 0, a, s);
+      if (tile.wgm == 2 && tile.wgn == 4) return launch_dma_epi<2, 4>(epi, tile.qt != 0, a, s);
       return hipErrorInvalidValue;
     }
     constexpr int DTv = DT_BF16;

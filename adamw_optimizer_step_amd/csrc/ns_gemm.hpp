@@ -54,8 +54,11 @@ struct NsArgs {
 constexpr int kNsPersBlocksPerXcd = 32;   // CUs per XCD
 
 // tile configuration chosen per launch: block tile bm x bn, K tile bk,
-// wgm x wgn waves; dma selects the LDS-DMA kernel (bf16, 256 x 256 x BK, 2 x 2 or 2 x 4 waves)
-struct NsTile { int bm, bn, bk, wgm, wgn, dma; };
+// wgm x wgn waves; dma selects the LDS-DMA kernel (bf16, 256 x 256 x BK, 2 x 2 or 2 x 4 waves);
+// qt (AXPY, 2 x 4 waves): Q = X^T is read from X (row-major) through
+// transposing LDS reads, so the iteration needs no X^T copy
+struct NsTile { int bm, bn, bk, wgm, wgn, dma, qt = 0; };
+
 
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& args, hipStream_t s);
 

@@ -63,21 +63,19 @@ def work_model(wl, ns_steps):
     gram = poly = axpy = 0.0
     gram_b = poly_b = axpy_b = 0.0
     pre = rown = post = 0.0
-    T = max(ns_steps, 1)
     for g in wl.muon_groups:
         m, n = min(g.rows, g.cols), max(g.rows, g.cols)
         gram += g.count * m * m * n          # A = X X^T, symmetric: m^2 n
         poly += g.count * m * m * m          # A A, symmetric: m^3
         axpy += g.count * 2.0 * m * m * n    # B X: 2 m^2 n
         # operands read once, outputs written once: GRAM reads X, writes A;
-        # POLY reads A, writes B; AXPY reads B and X^T and writes X' and X'^T
-        # (the last of the T launches writes one layout: mean per launch)
+        # POLY reads A, writes B; AXPY reads B and X, writes X'
         gram_b += g.count * (m * n + m * m) * ex
         poly_b += g.count * (2.0 * m * m) * ex
-        axpy_b += g.count * (m * m + m * n + m * n * (2.0 * T - 1.0) / T) * ex
+        axpy_b += g.count * (m * m + 2.0 * m * n) * ex
         e = g.rows * g.cols * g.count
         rown += e * (eg + em)                # read G, M
-        pre += e * (eg + 2 * em + 2 * ex)    # read G, M; write M, X0, X0^T
+        pre += e * (eg + 2 * em + ex)        # read G, M; write M, X0
         post += e * (2 * ep + ex)            # read W, U; write W
     adam = 28.0 * wl.adamw_numel
     return {
