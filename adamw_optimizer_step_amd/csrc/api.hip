@@ -142,9 +142,14 @@ void plan_group(GroupPlan& p, int64_t R, int64_t C, int count, int dt_x, size_t&
   p.x_stride = p.m_pad * p.n_pad;
   p.a_stride = p.m_pad * p.m_pad;
   p.row_stride = round_up(R, 64);
+  // X^T buffers: read by the fp32 iteration; in bf16 (AXPY reads X^T out of
+  // X) only a tall matrix uses them, as its parameter's layout. Otherwise
+  // they alias X and are never accessed.
+  const bool need_xt = p.tall || !ns_q_transposed(dt_x);
   for (int b = 0; b < 2; ++b) {
     p.off_x[b] = off;  off = align_up(off + (size_t)(count * p.x_stride * e), MA_WORKSPACE_ALIGN);
-    p.off_xt[b] = off; off = align_up(off + (size_t)(count * p.x_stride * e), MA_WORKSPACE_ALIGN);
+    p.off_xt[b] = p.off_x[b];
+    if (need_xt) { p.off_xt[b] = off; off = align_up(off + (size_t)(count * p.x_stride * e), MA_WORKSPACE_ALIGN); }
   }
   p.off_a = off;     off = align_up(off + (size_t)(count * p.a_stride * e), MA_WORKSPACE_ALIGN);
   p.off_b = off;     off = align_up(off + (size_t)(count * p.a_stride * e), MA_WORKSPACE_ALIGN);
@@ -847,7 +852,8 @@ int ma_test_ns(int64_t m, int64_t n, int32_t count, int32_t precision, const voi
     a.tiles_c = (int32_t)(p.c_ext / 64);
     a.x_stride = p.x_stride;
     a.xd = ws + p.off_x[0] + (size_t)(first * p.x_stride * e);
-    a.xt = ws + p.off_xt[0] + (size_t)(first * p.x_stride * e);
+    // m <= n: X^T is read only by the iteration without transposed AXPY reads
+    a.xt = ns_q_transposed(precision) ? nullptr : ws + p.off_xt[0] + (size_t)(first * p.x_stride * e);
     a.ld_d = p.n_pad;
     a.ld_t = p.m_pad;
     a.pure_copy = 1;
