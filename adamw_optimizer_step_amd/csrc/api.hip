@@ -91,6 +91,14 @@ bool ns_q_transposed(int dtype) {
   return !off && t.dma && t.wgm == 2 && t.wgn == 4 && t.bk == 64;
 }
 
+// Whether POLY writes only the upper triangle of B (no mirrored tiles), AXPY
+// reading the blocks left of the diagonal transposed from those above it:
+// with the transposed AXPY operands, unless MA_NS_SYMUP=0.
+bool ns_b_upper(int dtype) {
+  static const bool off = [] { const char* e = getenv("MA_NS_SYMUP"); return e && strcmp(e, "0") == 0; }();
+  return !off && ns_q_transposed(dtype);
+}
+
 NsTile ns_tile(int dtype, bool symmetric) {
   if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
   // the LDS-DMA kernel with 8 waves (2 x 4 of 128 x 64, two per SIMD); "dma"
@@ -306,6 +314,8 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
       NsTile tile = ns_tile(dtype, epi != EPI_AXPY);
       const bool qt = epi == EPI_AXPY && ns_q_transposed(dtype);
       tile.qt = qt ? 1 : 0;
+      // B is stored as its upper triangle when AXPY reads the rest transposed
+      const bool b_upper = ns_b_upper(dtype);
       if (epi != EPI_AXPY && tile.bm != tile.bn) return fail(MA_ERR_INVALID_ARG, "symmetric GEMM tile must be square");
       for (size_t base = 0; base < order.size(); base += kMaxNsGroups) {
         NsArgs A{};
@@ -336,6 +346,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.tm = G.tn = tm;
             G.tiles = tm * (tm + 1) / 2;
             G.symmetric = 1;
+            G.upper_only = epi == EPI_POLY && b_upper ? 1 : 0;
           } else {
             G.P = ws + p.off_b;
             G.sP = p.a_stride;
@@ -359,6 +370,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.tn = tn;
             G.tiles = tm * tn;
             G.symmetric = 0;
+            G.p_upper = b_upper ? 1 : 0;
           }
           G.unit = G.count >= 8 ? G.tiles : 1;
           G.rot = rot;

@@ -157,7 +157,9 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
   const int l32 = lane & 31, lh = lane >> 5;
   const int mat = J.mat, bi = J.bi, bj = J.bj;
   const bool diag = G.symmetric && bi == bj;
-  T* outT = reinterpret_cast<T*>(G.outT);
+  // a symmetric product writes its tile (bi, bj) and the mirror (bj, bi),
+  // the diagonal tiles once (transposed); upper_only drops the mirrors
+  T* outT = (G.symmetric && G.upper_only && !diag) ? nullptr : reinterpret_cast<T*>(G.outT);
   T* outN = diag ? nullptr : reinterpret_cast<T*>(G.outN);
 
   if constexpr (EPI != EPI_GRAM && !E_DONE) {
@@ -492,17 +494,19 @@ __device__ __forceinline__ void dma_wait_tiles(int tiles) {
 // Fragment reads of MFMA k-step kk (16 values of k) of a k-tile: this wave's
 // FM 32-row blocks of P (fa) and FN of Q (fb); lane (l32, lh) reads row l32
 // of each block at logical chunk 2 kk + lh.
-template <int WGM, int WGN, bool QT = false>
+template <int WGM, int WGN, bool QT = false, bool READ_P = true>
 __device__ __forceinline__ void dma_read_step(const unsigned char* cur, int kk, int lane, int wm, int wn,
                                               u32x4_t (&fa)[dma::Grid<WGM, WGN>::FM],
                                               u32x4_t (&fb)[dma::Grid<WGM, WGN>::FN]) {
   using namespace dma;
   using Gd = Grid<WGM, WGN>;
   const int l32 = lane & 31, c = kk * 2 + (lane >> 5);
+  if constexpr (READ_P) {
 #pragma unroll
-  for (int i = 0; i < Gd::FM; ++i) {
-    const int r = wm * Gd::WTM + i * 32 + l32;
-    fa[i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
+    for (int i = 0; i < Gd::FM; ++i) {
+      const int r = wm * Gd::WTM + i * 32 + l32;
+      fa[i] = *reinterpret_cast<const u32x4_t*>(cur + r * ROWB + ((c ^ swz(r)) << 4));
+    }
   }
   if constexpr (!QT) {
 #pragma unroll
@@ -544,6 +548,45 @@ __device__ __forceinline__ void qtr_read(const unsigned char* stage, const uint3
       : "memory");
   fb[0] = u32x4_t{r00.x, r00.y, r01.x, r01.y};
   fb[1] = u32x4_t{r10.x, r10.y, r11.x, r11.y};
+}
+
+// P and Q both read transposed (PT phase of AXPY): P's k-tile is 64 rows k of
+// the stored upper triangle of B (B[k][i] = B[i][k]) in the P half, laid out
+// like the Q half; poff[f] addresses fragment f (32 values i). Twelve reads,
+// one wait.
+template <int KK>
+__device__ __forceinline__ void pqtr_read(const unsigned char* stage, const uint32_t (&poff)[4], const uint32_t (&qoff)[2],
+                                          u32x4_t (&fa)[4], u32x4_t (&fb)[2]) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) const unsigned char lds_cu8_t;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_cu8_t*)stage;
+  u32x2_t p00, p01, p10, p11, p20, p21, p30, p31, q00, q01, q10, q11;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %2, %13 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %4, %14 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %6, %15 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%19\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:%21\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(p00), "=&v"(p01), "=&v"(p10), "=&v"(p11), "=&v"(p20), "=&v"(p21), "=&v"(p30), "=&v"(p31),
+        "=&v"(q00), "=&v"(q01), "=&v"(q10), "=&v"(q11)
+      : "v"(base + poff[0]), "v"(base + poff[1]), "v"(base + poff[2]), "v"(base + poff[3]),
+        "v"(base + QT_HALF + qoff[0]), "v"(base + QT_HALF + qoff[1]),
+        "i"(KK * 16 * 512), "i"((KK * 16 + 4) * 512), "i"(KK * 16 * 512), "i"((KK * 16 + 4) * 512)
+      : "memory");
+  fa[0] = u32x4_t{p00.x, p00.y, p01.x, p01.y};
+  fa[1] = u32x4_t{p10.x, p10.y, p11.x, p11.y};
+  fa[2] = u32x4_t{p20.x, p20.y, p21.x, p21.y};
+  fa[3] = u32x4_t{p30.x, p30.y, p31.x, p31.y};
+  fb[0] = u32x4_t{q00.x, q00.y, q01.x, q01.y};
+  fb[1] = u32x4_t{q10.x, q10.y, q11.x, q11.y};
 }
 
 // This wave's DMA of one k-tile (its panel of the stage: PANEL rows of P or
@@ -611,6 +654,14 @@ struct DmaCtx {
   int ld_src, lane, wm, wn, nk;
   int lane_off[2];
   uint32_t qoff[2];         // transposed Q fragment addresses (QT)
+  // P read transposed for k-tiles < pt_end (B stored as its upper triangle:
+  // the blocks left of the diagonal come from the blocks above it); the P
+  // waves' DMA uses the *_t source for those k-tiles
+  int pt_end, dma_t_end;
+  const uint16_t* src_t;
+  int64_t q_step_t, k_step_t;
+  int lane_off_t[2];
+  uint32_t poff[4];
   float a;
 };
 
@@ -623,7 +674,7 @@ struct DmaCtx {
 // Q = X^T) or A[i][j] (POLY, A symmetric) for them, so (a I) Q-block adds
 // a*X, or (b/c)*A, to the accumulators instead of reading it back in the
 // epilogue.
-template <int KKI, int IIB, int WGM, int WGN, bool QT>
+template <int KKI, int IIB, int WGM, int WGN, bool QT, bool PT>
 __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
                                           f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
                                           u32x4_t (&fa)[dma::Grid<WGM, WGN>::FM], u32x4_t (&fb)[dma::Grid<WGM, WGN>::FN],
@@ -637,7 +688,7 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
     // (read during the previous k-step) is not also a wait for the new reads
     mfma_rows<0, 1>(acc, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
-    dma_read_step<WGM, WGN, QT>(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
+    dma_read_step<WGM, WGN, QT, !PT>(c.smem + s_cur * STAGE_BYTES, KKI + 1, c.lane, c.wm, c.wn, na, nb);
     __builtin_amdgcn_sched_barrier(0);
     mfma_rows<1, FM>(acc, fa, fb);
   } else {
@@ -652,7 +703,9 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
       const int later = c.nk - 2 - kt;
       dma_wait_tiles<DPW>(later < STAGES - 2 ? later : STAGES - 2);
       __builtin_amdgcn_s_barrier();
-      dma_read_step<WGM, WGN, QT>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
+      // the next tile's P fragments, unless they are read transposed below
+      if (!PT || kt + 1 >= c.pt_end)
+        dma_read_step<WGM, WGN, QT>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, 0, c.lane, c.wm, c.wn, na, nb);
     }
     __builtin_amdgcn_sched_barrier(0);
     // the DMA of tile kt+STAGES into the stage just released, one instruction
@@ -660,24 +713,35 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
     // at the CU's one texture-address unit and hold up the MFMAs behind them
     const bool fill = kt + STAGES < c.nk;
     unsigned char* fill_at = c.wave_fill + s_cur * STAGE_BYTES;
-    const int64_t koff = (int64_t)(kt + STAGES) * c.k_step;
+    // the source layout of the tile being loaded (QT: the P waves' transposed
+    // source for the k-tiles left of the diagonal block)
+    const bool tsrc = QT && kt + STAGES < c.dma_t_end;
+    const uint16_t* src = tsrc ? c.src_t : c.src;
+    const int64_t q_step = tsrc ? c.q_step_t : c.q_step;
+    const int64_t koff = (int64_t)(kt + STAGES) * (tsrc ? c.k_step_t : c.k_step);
+    const int lo[2] = {tsrc ? c.lane_off_t[0] : c.lane_off[0], tsrc ? c.lane_off_t[1] : c.lane_off[1]};
 #pragma unroll
     for (int idx = 0; idx < FM * FN; ++idx) {
       mfma_frag<DT_BF16>(acc[idx / FN][idx % FN], fa[idx / FN], fb[idx % FN]);
 #pragma unroll
       for (int q = idx * DPW / (FM * FN); q < (idx + 1) * DPW / (FM * FN); ++q)
-        if (fill) dma_issue_one(fill_at, c.src, c.q_step, c.lane_off, koff, q);
+        if (fill) dma_issue_one(fill_at, src, q_step, lo, koff, q);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (IIB >= 0) ident_step<IIB + KKI / 2>(acc, fb, KKI % 2, c.lane, c.a);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (QT) {
-    // the next k-step's Q fragments, after this k-step's MFMAs are queued
+    // the next k-step's Q fragments (and, transposed, P's), after this
+    // k-step's MFMAs are queued
     if constexpr (KKI + 1 < KK) {
-      qtr_read<KKI + 1>(c.smem + s_cur * STAGE_BYTES, c.qoff, nb);
+      if constexpr (PT) pqtr_read<KKI + 1>(c.smem + s_cur * STAGE_BYTES, c.poff, c.qoff, na, nb);
+      else qtr_read<KKI + 1>(c.smem + s_cur * STAGE_BYTES, c.qoff, nb);
     } else {
-      if (kt + 1 < c.nk) qtr_read<0>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, c.qoff, nb);
+      if (kt + 1 < c.nk) {
+        if (PT && kt + 1 < c.pt_end) pqtr_read<0>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, c.poff, c.qoff, na, nb);
+        else qtr_read<0>(c.smem + ((kt + 1) % STAGES) * STAGE_BYTES, c.qoff, nb);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -685,16 +749,16 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
 
 // One k-tile: KK k-steps, the fragment sets alternating (0, 1) -> (1, 0) -> ...
 // so that (f0a, f0b) again hold the next tile's first k-step afterwards.
-template <int IIB, int WGM, int WGN, bool QT>
+template <int IIB, int WGM, int WGN, bool QT, bool PT = false>
 __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
                                           f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
                                           u32x4_t (&f0a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f0b)[dma::Grid<WGM, WGN>::FN],
                                           u32x4_t (&f1a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f1b)[dma::Grid<WGM, WGN>::FN]) {
-  dma_kstep<0, IIB, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
-  dma_kstep<1, IIB, WGM, WGN, QT>(c, kt, acc, f1a, f1b, f0a, f0b);
+  dma_kstep<0, IIB, WGM, WGN, QT, PT>(c, kt, acc, f0a, f0b, f1a, f1b);
+  dma_kstep<1, IIB, WGM, WGN, QT, PT>(c, kt, acc, f1a, f1b, f0a, f0b);
   if constexpr (dma::KK == 4) {
-    dma_kstep<2, IIB, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
-    dma_kstep<3, IIB, WGM, WGN, QT>(c, kt, acc, f1a, f1b, f0a, f0b);
+    dma_kstep<2, IIB, WGM, WGN, QT, PT>(c, kt, acc, f0a, f0b, f1a, f1b);
+    dma_kstep<3, IIB, WGM, WGN, QT, PT>(c, kt, acc, f1a, f1b, f0a, f0b);
   }
 }
 
@@ -756,6 +820,8 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
     for (int par = 0; par < 2; ++par)
       c.lane_off[par] = (lane / CPR) * c.ld_src + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
   }
+  c.pt_end = 0;
+  c.dma_t_end = 0;
   if constexpr (QT) {
     // transposed Q fragment addresses (see qtr_read)
     const int g = lane >> 4, a4 = (lane >> 2) & 3, b4 = lane & 3;
@@ -763,6 +829,27 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
     for (int j = 0; j < 2; ++j) {
       const int chunk = (c.wn * Gd::WTN + j * 32) / 8 + 2 * (g & 1) + (b4 >> 1);
       c.qoff[j] = (uint32_t)((8 * (g >> 1) + a4) * 512 + ((chunk ^ (4 * a4)) << 4) + (b4 & 1) * 8);
+    }
+    if (G.p_upper) {
+      // P = B stored as its upper triangle: for k < bi*BM, B[i][k] = B[k][i]
+      // is read transposed from the block above the diagonal, rows k of
+      // columns bi*BM .. +BM, exactly as Q is (P half, same swizzle)
+      c.pt_end = J.bi * (BM / BK);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int chunk = (c.wm * Gd::WTM + f * 32) / 8 + 2 * (g & 1) + (b4 >> 1);
+        c.poff[f] = (uint32_t)((8 * (g >> 1) + a4) * 512 + ((chunk ^ (4 * a4)) << 4) + (b4 & 1) * 8);
+      }
+      if (isP) {
+        c.dma_t_end = c.pt_end;
+        c.src_t = reinterpret_cast<const uint16_t*>(G.P) + (int64_t)J.mat * G.sP + (int64_t)(wave * 16) * c.ld_src +
+                  (int64_t)J.bi * BM;
+        c.q_step_t = 2 * (int64_t)c.ld_src;
+        c.k_step_t = (int64_t)BK * c.ld_src;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+          c.lane_off_t[par] = (lane >> 5) * c.ld_src + (((lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3))) << 3);
+      }
     }
   }
 
@@ -779,14 +866,29 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   // and each k-step's fragments are read while the previous k-step's MFMAs
   // run.
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t)
-    dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.q_step, c.lane_off, (int64_t)t * c.k_step);
+  for (int t = 0; t < STAGES; ++t) {
+    if (QT && t < c.dma_t_end)
+      dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src_t, c.q_step_t, c.lane_off_t, (int64_t)t * c.k_step_t);
+    else
+      dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.q_step, c.lane_off, (int64_t)t * c.k_step);
+  }
   dma_wait_tiles<DPW>(STAGES - 1);   // this wave's part of tile 0 has landed
   __builtin_amdgcn_s_barrier();
   u32x4_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
-  dma_read_step<WGM, WGN, QT>(smem, 0, lane, c.wm, c.wn, f0a, f0b);
-  if constexpr (QT) qtr_read<0>(smem, c.qoff, f0b);
   int kt = 0;
+  if constexpr (QT) {
+    if (c.pt_end > 0) {
+      pqtr_read<0>(smem, c.poff, c.qoff, f0a, f0b);
+    } else {
+      dma_read_step<WGM, WGN, QT>(smem, 0, lane, c.wm, c.wn, f0a, f0b);
+      qtr_read<0>(smem, c.qoff, f0b);
+    }
+    // the k-tiles left of the diagonal block, P read transposed (none of
+    // them carries the folded term: those start at bi*BM)
+    for (; kt < c.pt_end; ++kt) dma_ktile<-1, WGM, WGN, QT, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+  } else {
+    dma_read_step<WGM, WGN, QT>(smem, 0, lane, c.wm, c.wn, f0a, f0b);
+  }
   if constexpr (FOLD) {
     // the k-tiles whose k range is this wave's 128 output rows (K = m_pad,
     // so they lie inside [0, nk)) carry the a*X (AXPY) or (b/c)*A (POLY)

@@ -31,6 +31,11 @@ struct NsGroup {
   int32_t unit;       // jobs per scheduling unit: tiles (whole matrix) or 1 (one tile)
   int32_t rot;        // unit u of this group goes to XCD (u + rot) % 8
   int32_t symmetric;  // 1: only tiles bi <= bj, mirrored through outN/outT
+  int32_t upper_only; // symmetric: write each tile once (no mirror); the
+                      // lower triangle of the output is left unwritten
+  int32_t p_upper;    // AXPY with qt: P holds only its upper triangle (B
+                      // symmetric); blocks left of the diagonal are read
+                      // transposed from those above it
 };
 
 // Scheduling: the hardware deals consecutive workgroups round-robin to the 8
