@@ -130,6 +130,23 @@ __device__ __forceinline__ bool map_job(const NsArgs& args, TileJob& J) {
 // ---------------------------------------------------------------------------
 // epilogue: a/b/c combination, then staged, coalesced stores
 // ---------------------------------------------------------------------------
+// registers 4q..4q+3 of an accumulator block to 4 staging rows, one element
+// each (stride `ld` elements)
+template <int DT>
+__device__ __forceinline__ void stage4_strided(typename MfmaTraits<DT>::T* p, int ld, const f32x16_t& a, int q) {
+  if constexpr (DT == DT_BF16) {
+    const uint32_t p01 = pack_bf16x2(a[4 * q], a[4 * q + 1]);
+    const uint32_t p23 = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
+    p[0] = (uint16_t)(p01 & 0xFFFFu);
+    p[ld] = (uint16_t)(p01 >> 16);
+    p[2 * ld] = (uint16_t)(p23 & 0xFFFFu);
+    p[3 * ld] = (uint16_t)(p23 >> 16);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r * ld] = a[4 * q + r];
+  }
+}
+
 template <int DT, int BM, int BN>
 struct EpiSmem {
   using Tr = MfmaTraits<DT>;
@@ -139,9 +156,12 @@ struct EpiSmem {
 };
 
 // Accumulator layout of a 32x32 MFMA block: lane l holds column (l % 32) and,
-// in registers 4q..4q+3, rows 8q + 4(l/32) + 0..3. The caller has finished
-// with LDS (a barrier precedes the call).
-template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false>
+// in registers 4q..4q+3, rows 8q + 4(l/32) + 0..3. ACC_T: the block was
+// accumulated transposed (operands swapped in the MFMA), so lane l holds row
+// (l % 32) and columns 8q + 4(l/32) + 0..3; row-major staging then writes 8
+// bytes per lane, the transposed staging 2. The caller has finished with LDS
+// (a barrier precedes the call).
+template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false, bool ACC_T = false>
 __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
                                             unsigned char* smem, int tid_in = -1) {
@@ -158,24 +178,38 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
   const int mat = J.mat, bi = J.bi, bj = J.bj;
   const bool diag = G.symmetric && bi == bj;
   // a symmetric product writes its tile (bi, bj) and the mirror (bj, bi),
-  // the diagonal tiles once (transposed); upper_only drops the mirrors
-  T* outT = (G.symmetric && G.upper_only && !diag) ? nullptr : reinterpret_cast<T*>(G.outT);
-  T* outN = diag ? nullptr : reinterpret_cast<T*>(G.outN);
+  // the diagonal tiles once (in the layout whose staging is cheaper: the
+  // two are the same block, of the same buffer); upper_only drops the mirrors
+  T* outT = ((ACC_T && diag) || (G.symmetric && G.upper_only && !diag)) ? nullptr : reinterpret_cast<T*>(G.outT);
+  T* outN = (!ACC_T && diag) ? nullptr : reinterpret_cast<T*>(G.outN);
+  // (il, jl): the output row and column of register 4q of block (i, j)
+  auto rc = [&](int i, int j, int q, int& il, int& jl) __attribute__((always_inline)) {
+    if constexpr (ACC_T) {
+      il = wm * WTM + i * 32 + l32;
+      jl = wn * WTN + j * 32 + q * 8 + lh * 4;
+    } else {
+      il = wm * WTM + i * 32 + q * 8 + lh * 4;
+      jl = wn * WTN + j * 32 + l32;
+    }
+  };
 
   if constexpr (EPI != EPI_GRAM && !E_DONE) {
     // E[j][i..i+3]: A (symmetric) for POLY, X^T for AXPY; one 32x32 block at
-    // a time, so that the loads of all blocks are not held in registers at once
+    // a time, so that the loads of all blocks are not held in registers at once.
+    // ACC_T reads E[i][j..j+3], which is the same value only for symmetric A.
+    static_assert(!ACC_T || EPI == EPI_POLY, "transposed accumulators read E as a symmetric matrix");
     const T* Eg = reinterpret_cast<const T*>(G.E) + (int64_t)mat * G.sE;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int jl = wn * WTN + j * 32 + l32;
         float e[4][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int il = wm * WTM + i * 32 + q * 8 + lh * 4;
-          const T* ep = Eg + (int64_t)(bj * BN + jl) * G.ldE + bi * BM + il;
+          int il, jl;
+          rc(i, j, q, il, jl);
+          const T* ep = ACC_T ? Eg + (int64_t)(bi * BM + il) * G.ldE + bj * BN + jl
+                              : Eg + (int64_t)(bj * BN + jl) * G.ldE + bi * BM + il;
           if constexpr (DT == DT_BF16) {
             const uint2 u = *reinterpret_cast<const uint2*>(ep);
             e[q][0] = __uint_as_float(u.x << 16); e[q][1] = __uint_as_float(u.x & 0xFFFF0000u);
@@ -214,11 +248,13 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int jl = wn * WTN + j * 32 + l32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int il = wm * WTM + i * 32 + q * 8 + lh * 4;
-          if constexpr (DT == DT_BF16) {
+          int il, jl;
+          rc(i, j, q, il, jl);
+          if constexpr (ACC_T) {
+            stage4_strided<DT>(stg + jl * ES::LDT + il, ES::LDT, acc[i][j], q);
+          } else if constexpr (DT == DT_BF16) {
             uint2 u;
             u.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
             u.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
@@ -246,20 +282,20 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int jl = wn * WTN + j * 32 + l32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int il = wm * WTM + i * 32 + q * 8 + lh * 4;
-          if constexpr (DT == DT_BF16) {
-            const uint32_t p01 = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            const uint32_t p23 = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            stg[(il + 0) * ES::LDN + jl] = (uint16_t)(p01 & 0xFFFFu);
-            stg[(il + 1) * ES::LDN + jl] = (uint16_t)(p01 >> 16);
-            stg[(il + 2) * ES::LDN + jl] = (uint16_t)(p23 & 0xFFFFu);
-            stg[(il + 3) * ES::LDN + jl] = (uint16_t)(p23 >> 16);
+          int il, jl;
+          rc(i, j, q, il, jl);
+          if constexpr (!ACC_T) {
+            stage4_strided<DT>(stg + il * ES::LDN + jl, ES::LDN, acc[i][j], q);
+          } else if constexpr (DT == DT_BF16) {
+            uint2 u;
+            u.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            u.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<uint2*>(stg + il * ES::LDN + jl) = u;
           } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) stg[(il + r) * ES::LDN + jl] = acc[i][j][4 * q + r];
+            *reinterpret_cast<float4*>(stg + il * ES::LDN + jl) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           }
         }
       }
@@ -612,18 +648,27 @@ __device__ __forceinline__ void dma_issue_one(unsigned char* fill, const uint16_
   __builtin_amdgcn_global_load_lds(src + q * q_step + lane_off[q & 1] + koff, (lds_void_t*)(fill + q * 1024), 16, 0, 0);
 }
 
+// acc += P-block Q-block^T, accumulated transposed: with Q as the MFMA's
+// first operand each lane holds 4 consecutive columns of one output row, so
+// the row-major output is staged 8 bytes per lane (the product of each pair
+// of values, and the order of the sums, are the same either way)
+__device__ __forceinline__ void mfma_pq(f32x16_t& acc, const u32x4_t& p, const u32x4_t& q) {
+  mfma_frag<DT_BF16>(acc, q, p);
+}
+
 // MFMAs of one k-step for accumulator rows [I0, I1)
 template <int I0, int I1, int FM, int FN>
 __device__ __forceinline__ void mfma_rows(f32x16_t (&acc)[FM][FN], const u32x4_t (&fa)[FM], const u32x4_t (&fb)[FN]) {
 #pragma unroll
   for (int i = I0; i < I1; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) mfma_frag<DT_BF16>(acc[i][j], fa[i], fb[j]);
+    for (int j = 0; j < FN; ++j) mfma_pq(acc[i][j], fa[i], fb[j]);
 }
 
 // acc[II][j] += (a I) X^T-block for k-step h (0 or 1) of row block II, with
 // a = a_hi + a_lo (both exact in bf16). Lane (l32, lh) holds k = 16 h + 8 lh + e
-// of the block, and row i = l32 of a I is nonzero only at k = i.
+// of the block, and row i = l32 of a I is nonzero only at k = i (the same
+// registers serve as either MFMA operand: a I is symmetric).
 template <int II, int FM, int FN>
 __device__ __forceinline__ void ident_step(f32x16_t (&acc)[FM][FN], const u32x4_t (&fb)[FN], int h, int lane,
                                            float a_coef) {
@@ -641,8 +686,8 @@ __device__ __forceinline__ void ident_step(f32x16_t (&acc)[FM][FN], const u32x4_
   }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    mfma_frag<DT_BF16>(acc[II][j], id_hi, fb[j]);
-    mfma_frag<DT_BF16>(acc[II][j], id_lo, fb[j]);
+    mfma_pq(acc[II][j], id_hi, fb[j]);
+    mfma_pq(acc[II][j], id_lo, fb[j]);
   }
 }
 
@@ -722,7 +767,7 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
     const int lo[2] = {tsrc ? c.lane_off_t[0] : c.lane_off[0], tsrc ? c.lane_off_t[1] : c.lane_off[1]};
 #pragma unroll
     for (int idx = 0; idx < FM * FN; ++idx) {
-      mfma_frag<DT_BF16>(acc[idx / FN][idx % FN], fa[idx / FN], fb[idx % FN]);
+      mfma_pq(acc[idx / FN][idx % FN], fa[idx / FN], fb[idx % FN]);
 #pragma unroll
       for (int q = idx * DPW / (FM * FN); q < (idx + 1) * DPW / (FM * FN); ++q)
         if (fill) dma_issue_one(fill_at, src, q_step, lo, koff, q);
@@ -907,7 +952,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD>(args, G, J, acc, smem, tid);
+  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true>(args, G, J, acc, smem, tid);
 }
 
 // Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
