@@ -67,6 +67,7 @@ EXPORTS = {
                                C.c_size_t, C.c_void_p]),
     "ma_muon_step_stats": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
                                      C.c_size_t, C.c_void_p, C.c_void_p]),
+    "ma_muon_row_pass": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_int32]),
     "ma_muon_workspace_update": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC),
                                            C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_void_p),
                                            C.POINTER(C.c_int64), C.POINTER(C.c_int32),

@@ -160,6 +160,18 @@ def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[
     return workspace
 
 
+def muon_row_pass(groups: Sequence[MuonGroup], hp: MuonHParams, group: int) -> bool:
+    """Whether ``muon_step`` reads group ``group``'s G and M once (momentum,
+    MuonEq row sums and X0 in one pass, the Frobenius factor applied by the
+    first Newton-Schulz products) rather than twice (``ma_muon_row_pass``)."""
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    rc = L.lib().ma_muon_row_pass(garr, len(groups), C.byref(h), group)
+    if rc < 0:
+        L.check(rc)
+    return rc == 1
+
+
 def muon_workspace_update(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: torch.Tensor,
                           group: int, index: int) -> torch.Tensor:
     """View of the update U of one matrix inside ``workspace`` (parameter layout)."""

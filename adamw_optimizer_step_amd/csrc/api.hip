@@ -99,6 +99,7 @@ bool ns_b_upper(int dtype) {
   return !off && ns_q_transposed(dtype);
 }
 
+
 NsTile ns_tile(int dtype, bool symmetric) {
   if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
   // the LDS-DMA kernel with 8 waves (2 x 4 of 128 x 64, two per SIMD); "dma"
@@ -256,6 +257,16 @@ int build_plan(const ma_muon_group* groups, int32_t n, const ma_muon_hparams* hp
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// C % 8 == 0 and every parameter, gradient and momentum buffer of the group
+// 16-byte aligned: the elementwise kernels' vector path
+bool group_vec(const GroupPlan& p) {
+  bool vec = (p.C % 8) == 0;
+  if (p.src)
+    for (int k = 0; k < p.count; ++k)
+      vec = vec && aligned16(p.src->grads[k]) && aligned16(p.src->momentum[k]) && aligned16(p.src->params[k]);
+  return vec;
+}
+
 ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char* ws, int first,
                    int cnt) {
   ElemArgs a{};
@@ -284,21 +295,21 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
   a.norm_eps = hp->norm_eps;
   a.eq_eps = hp->eq_eps;
   a.finalize_mode = hp->equilibrate == MA_EQ_ROWS_PRE ? 1 : 0;
-  bool vec = (p.C % 8) == 0;
   for (int i = 0; i < cnt; ++i) {
     const int k = first + i;
     a.mat[i].g = p.src ? p.src->grads[k] : nullptr;
     a.mat[i].m = p.src ? p.src->momentum[k] : nullptr;
     a.mat[i].w = p.src ? p.src->params[k] : nullptr;
-    if (p.src) vec = vec && aligned16(a.mat[i].g) && aligned16(a.mat[i].m) && aligned16(a.mat[i].w);
   }
-  a.vec = vec ? 1 : 0;
+  a.vec = group_vec(p) ? 1 : 0;
   return a;
 }
 
 // Enqueue T quintic steps for every group of the plan; X[0]/X^T[0] hold X0.
+// scaled (optional): per group, whether X0 holds Y with X0 = s Y, s in the
+// group's row-factor slot of row 0 of each matrix (k_finalize mode 4).
 int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
-               hipStream_t s) {
+               hipStream_t s, const std::vector<char>* scaled = nullptr) {
   if (T == 0 || plan.g.empty()) return MA_OK;
   // groups with the most work per tile first (they set the tail of a launch)
   std::vector<int> order;
@@ -372,6 +383,10 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.symmetric = 0;
             G.p_upper = b_upper ? 1 : 0;
           }
+          // the first GRAM and AXPY apply the deferred Frobenius factor
+          const bool sc = step == 0 && epi != EPI_POLY && scaled && (*scaled)[order[base + q]];
+          G.scale = sc ? reinterpret_cast<const float*>(ws + p.off_rowf) : nullptr;
+          G.scale_stride = p.row_stride;
           G.unit = G.count >= 8 ? G.tiles : 1;
           G.rot = rot;
           rot = (rot + G.count * G.tiles / G.unit) & 7;
@@ -471,6 +486,18 @@ size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups, con
   return plan.bytes;
 }
 
+// Whether a group's momentum update, row sums and X0 run as one row pass
+// (k_pre_rows), the Frobenius factor then applied by the first GRAM and AXPY:
+// MuonEq pre with at least one Newton-Schulz step, a matrix whose iteration
+// layout is the parameter's (no more rows than columns), an iteration that
+// needs no X0^T (AXPY reads X^T out of X) and rows the pass holds in
+// registers; unless MA_PRE_ROWS=0.
+bool pre_rows_for(const GroupPlan& p, const ma_muon_hparams* hp) {
+  static const bool off = [] { const char* e = getenv("MA_PRE_ROWS"); return e && strcmp(e, "0") == 0; }();
+  return !off && hp->equilibrate == MA_EQ_ROWS_PRE && hp->ns_steps > 0 && !p.tall && ns_q_transposed(p.dt_x) &&
+         group_vec(p) && p.C <= kPreRowsMaxCols && p.c_ext <= kPreRowsMaxCols && p.ld_direct() % 8 == 0;
+}
+
 namespace {
 int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
                    size_t workspace_bytes, float* stats, void* stream) {
@@ -505,11 +532,24 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   hipError_t err;
-  // 1. norms, 2. factors, 3. momentum update and X0 (both layouts)
-  for (const GroupPlan& p : plan.g) {
+  // 1. norms, 2. factors, 3. momentum update and X0 (both layouts); or the
+  // row pass (momentum, norms, row-scaled X0) and the Frobenius factor alone
+  std::vector<char> scaled(plan.g.size(), 0);
+  for (size_t gi = 0; gi < plan.g.size(); ++gi) {
+    const GroupPlan& p = plan.g[gi];
     for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
       const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
       ElemArgs a = elem_args(p, hp, ws, first, cnt);
+      if (first == 0) scaled[gi] = pre_rows_for(p, hp) ? 1 : 0;
+      if (scaled[gi]) {
+        // a.xd is X0 in the parameter's layout, which is the iteration's
+        { ProfScope ps(MA_K_PRE, s); err = launch_pre_rows(p.dt_g, p.dt_m, p.dt_x, a, s); }
+        if (err != hipSuccess) return hip_fail(err, "momentum/row norms/X0");
+        a.finalize_mode = 4;
+        { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
+        if (err != hipSuccess) return hip_fail(err, "norm finalize");
+        continue;
+      }
       { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_momentum(p.dt_g, p.dt_m, a, s); }
       if (err != hipSuccess) return hip_fail(err, "row norms");
       { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
@@ -527,7 +567,7 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
     }
   }
   // 4. T quintic steps
-  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s);
+  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s, &scaled);
   if (rc) return rc;
   // 5. (MuonEq POST) and the update (and the update norms)
   const int ub = hp->ns_steps & 1;
@@ -573,6 +613,14 @@ int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_m
                        void* workspace, size_t workspace_bytes, float* stats, void* stream) {
   if (!stats || ((uintptr_t)stats & 3)) return fail(MA_ERR_INVALID_ARG, "stats is null or not 4-byte aligned");
   return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, stats, stream);
+}
+
+int ma_muon_row_pass(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, int32_t group) {
+  Plan plan;
+  int rc = build_plan(groups, n_groups, hp, plan, false);
+  if (rc) return rc;
+  if (group < 0 || group >= n_groups) return fail(MA_ERR_INVALID_ARG, "group %d out of range", group);
+  return pre_rows_for(plan.g[group], hp) ? 1 : 0;
 }
 
 int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,

@@ -1,8 +1,9 @@
 // Muon elementwise and reduction kernels (gfx950), HBM-bound.
 //
 //   k_rowsumsq_momentum  per row of the Nesterov look-ahead Mt = G + beta*m1,
-//                        m1 = beta*M + G: sum of squares (one wave per row,
-//                        16-byte loads, butterfly shuffle reduction; no atomics)
+//                        m1 = beta*M + G: sum of squares (a wave per 4 rows,
+//                        up to 16 16-byte loads per lane in flight, butterfly
+//                        shuffle reduction; no atomics)
 //   k_finalize           per matrix: Frobenius scale, MuonEq row factors,
 //                        NorMuon row factors
 //   k_pre                momentum update M <- m1 (stored), X0 = Mt * f_row,
@@ -43,52 +44,97 @@ __device__ __forceinline__ void momentum1(float g, float m, float beta, int nest
 
 constexpr int kRowsPerBlock = 16;
 
-template <int DTG, int DTM>
+// 8 elements of a 16-byte-aligned run, as loaded (two 16-byte words for
+// fp32, one for bf16), unpacked only when used
+template <int DT>
+struct Raw8 {
+  uint4 w[DT == DT_BF16 ? 1 : 2];
+};
+template <int DT>
+__device__ __forceinline__ void raw_load(const void* p, Raw8<DT>& r) {
+#pragma unroll
+  for (int i = 0; i < (DT == DT_BF16 ? 1 : 2); ++i) r.w[i] = reinterpret_cast<const uint4*>(p)[i];
+}
+template <int DT>
+__device__ __forceinline__ float raw_at(const Raw8<DT>& r, int e) {
+  if constexpr (DT == DT_BF16) {
+    const uint32_t w = r.w[0][e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    return __uint_as_float(r.w[e >> 2][e & 3]);
+  }
+}
+
+// A wave owns 4 consecutive rows of its block's 16. Vector path: the row's
+// 512-element chunks (8 per lane) are read CPB at a time for RB rows at once,
+// 8 chunks of G and 8 of M per lane in flight, kept packed until used; each
+// lane adds its elements in column order, so the sums do not depend on CPB.
+template <int DTG, int DTM, int CPB>
 __global__ void __launch_bounds__(256) k_rowsumsq_momentum(const ElemArgs a) {
+  constexpr int RB = 8 / CPB < 4 ? 8 / CPB : 4;   // rows per batch
+  constexpr int NS = RB * CPB;                     // chunk slots per operand
   const int bpm = (a.R + kRowsPerBlock - 1) / kRowsPerBlock;
   const int k = blockIdx.x / bpm;
   const int rb = blockIdx.x - k * bpm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const void* gp = a.mat[k].g;
   const void* mp = a.mat[k].m;
-  for (int rr = wave; rr < kRowsPerBlock; rr += 4) {
-    const int r = rb * kRowsPerBlock + rr;
-    if (r >= a.R) break;
-    const int64_t base = (int64_t)r * a.C;
-    float acc = 0.0f;
-    if (a.vec) {
-      // up to 4 chunks of 8 per lane in flight before any arithmetic
-      for (int c0 = lane * 8; c0 < a.C; c0 += 4 * 512) {
-        float g[4][8], m[4][8];
+  const int row0 = rb * kRowsPerBlock + wave * 4;
+  if (a.vec) {
+    const int cpr = (a.C + 511) >> 9;
+#pragma unroll 1
+    for (int rr = 0; rr < 4; rr += RB) {
+      float acc[RB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = c0 + u * 512;
-          if (c < a.C) {
-            load8<DTG>(eptr<DTG>(gp, base + c), g[u]);
-            load8<DTM>(eptr<DTM>(mp, base + c), m[u]);
-          }
+      for (int q = 0; q < RB; ++q) acc[q] = 0.0f;
+#pragma unroll 1
+      for (int c0 = 0; c0 < cpr; c0 += CPB) {
+        Raw8<DTG> g[NS];
+        Raw8<DTM> m[NS];
+        // every slot loads (out-of-range slots re-read the matrix's first
+        // chunk and add nothing), so that all loads issue back to back
+        bool ok[NS];
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const int r = row0 + rr + u / CPB, c = (c0 + u % CPB) * 512 + lane * 8;
+          ok[u] = r < a.R && c < a.C;
+          const int64_t off = ok[u] ? (int64_t)r * a.C + c : 0;
+          raw_load<DTG>(eptr<DTG>(gp, off), g[u]);
+          raw_load<DTM>(eptr<DTM>(mp, off), m[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (c0 + u * 512 < a.C) {
+        for (int u = 0; u < NS; ++u) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float m1, mt;
-              momentum1(g[u][e], m[u][e], a.beta, a.nesterov, m1, mt);
-              acc = __builtin_fmaf(mt, mt, acc);
-            }
+          for (int e = 0; e < 8; ++e) {
+            float m1, mt;
+            momentum1(raw_at<DTG>(g[u], e), raw_at<DTM>(m[u], e), a.beta, a.nesterov, m1, mt);
+            const float t = __builtin_fmaf(mt, mt, acc[u / CPB]);
+            acc[u / CPB] = ok[u] ? t : acc[u / CPB];
           }
         }
       }
-    } else {
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const float t = wave_sum(acc[q]);
+        const int r = row0 + rr + q;
+        if (lane == 0 && r < a.R) a.rowsq[(int64_t)k * a.row_stride + r] = t;
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      const int r = row0 + q;
+      if (r >= a.R) break;
+      const int64_t base = (int64_t)r * a.C;
+      float acc = 0.0f;
       for (int c = lane; c < a.C; c += 64) {
         float m1, mt;
         momentum1(load1<DTG>(gp, base + c), load1<DTM>(mp, base + c), a.beta, a.nesterov, m1, mt);
         acc = __builtin_fmaf(mt, mt, acc);
       }
+      acc = wave_sum(acc);
+      if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = acc;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = acc;
   }
 }
 
@@ -130,7 +176,7 @@ __global__ void __launch_bounds__(256) k_finalize(const ElemArgs a) {
   float part = 0.0f;
   for (int i = t; i < a.R; i += 256) {
     const float q = rs[i];
-    if (mode == 1) {
+    if (mode == 1 || mode == 4) {
       const float n = sqrtf(q);
       const float y = n / (n + a.eq_eps);   // norm of the equilibrated row
       part += y * y;
@@ -151,6 +197,10 @@ __global__ void __launch_bounds__(256) k_finalize(const ElemArgs a) {
   } else if (mode == 1) {
     const float s = 1.0f / (sqrtf(total) + a.norm_eps);
     for (int i = t; i < a.R; i += 256) rf[i] = s / (sqrtf(rs[i]) + a.eq_eps);
+  } else if (mode == 4) {
+    // MuonEq pre with the row factors already applied (k_pre_rows): only the
+    // matrix's Frobenius factor, in the row-factor slot of row 0
+    if (t == 0) rf[0] = 1.0f / (sqrtf(total) + a.norm_eps);
   } else if (mode == 2) {
     const float rho = sqrtf(total) / sqrtf((float)a.R);
     for (int i = t; i < a.R; i += 256) rf[i] = rho / (sqrtf(rs[i]) + a.eq_eps);
@@ -244,6 +294,73 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = tile[rr + e][cc];
       store8<DTX>(eptr<DTX>(xt, (int64_t)(c0 + cc) * a.ld_t + r0 + rr), y);
+    }
+  }
+}
+
+// One wave per row of a matrix with no more rows than columns (its
+// iteration layout is the parameter's): M <- m1, the row's sum of squares of
+// Mt (summed in the order k_rowsumsq_momentum uses) and the X0 row
+// Mt / (||Mt_row|| + eq_eps), the MuonEq row scaling, with the padding
+// columns and rows of the iteration buffer zeroed. The matrix's Frobenius
+// factor (k_finalize mode 4) is applied by the first Newton-Schulz products
+// instead, so G and M are read once. Vector path only (C % 8 == 0, aligned),
+// C <= 512 CH.
+template <int DTG, int DTM, int DTX, int CH>
+__global__ void __launch_bounds__(256) k_pre_rows(const ElemArgs a) {
+  const int bpm = (a.r_ext + 3) >> 2;
+  const int k = blockIdx.x / bpm;
+  const int r = (blockIdx.x - k * bpm) * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= a.r_ext) return;
+  void* xd = eptr<DTX>(a.xd, (int64_t)k * a.x_stride);
+  const int64_t xrow = (int64_t)r * a.ld_d;
+  if (r >= a.R) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int c = u * 512 + lane * 8;
+      float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (c < a.c_ext) store8<DTX>(eptr<DTX>(xd, xrow + c), z);
+    }
+    return;
+  }
+  const void* gp = a.mat[k].g;
+  void* mp = a.mat[k].m;
+  Raw8<DTG> g[CH];
+  Raw8<DTM> m[CH];
+  bool ok[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int c = u * 512 + lane * 8;
+    ok[u] = c < a.C;
+    const int64_t off = ok[u] ? (int64_t)r * a.C + c : 0;
+    raw_load<DTG>(eptr<DTG>(gp, off), g[u]);
+    raw_load<DTM>(eptr<DTM>(static_cast<const void*>(mp), off), m[u]);
+  }
+  float mt[CH][8];
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    float m1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      momentum1(raw_at<DTG>(g[u], e), raw_at<DTM>(m[u], e), a.beta, a.nesterov, m1[e], mt[u][e]);
+      const float t = __builtin_fmaf(mt[u][e], mt[u][e], acc);
+      acc = ok[u] ? t : acc;
+    }
+    if (ok[u]) store8<DTM>(eptr<DTM>(mp, (int64_t)r * a.C + u * 512 + lane * 8), m1);
+  }
+  const float n2 = wave_sum(acc);
+  if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = n2;
+  const float f = 1.0f / (sqrtf(n2) + a.eq_eps);
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int c = u * 512 + lane * 8;
+    if (c < a.c_ext) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = ok[u] ? __fmul_rn(mt[u][e], f) : 0.0f;
+      store8<DTX>(eptr<DTX>(xd, xrow + c), x);
     }
   }
 }
@@ -413,10 +530,49 @@ __global__ void __launch_bounds__(256) k_bf16_round(const float* in, uint16_t* o
     else hipLaunchKernelGGL((KER<DT_F32, DT_F32>), __VA_ARGS__);                         \
   } while (0)
 
+#define MA_DISPATCH2C(d1, d2, KER, C3, ...)                                                       \
+  do {                                                                                            \
+    if ((d1) == DT_BF16 && (d2) == DT_BF16) hipLaunchKernelGGL((KER<DT_BF16, DT_BF16, C3>), __VA_ARGS__); \
+    else if ((d1) == DT_BF16) hipLaunchKernelGGL((KER<DT_BF16, DT_F32, C3>), __VA_ARGS__);        \
+    else if ((d2) == DT_BF16) hipLaunchKernelGGL((KER<DT_F32, DT_BF16, C3>), __VA_ARGS__);        \
+    else hipLaunchKernelGGL((KER<DT_F32, DT_F32, C3>), __VA_ARGS__);                               \
+  } while (0)
+
 hipError_t launch_rowsumsq_momentum(int dt_g, int dt_m, const ElemArgs& a, hipStream_t s) {
   const int blocks = a.count * ((a.R + kRowsPerBlock - 1) / kRowsPerBlock);
   if (blocks <= 0) return hipSuccess;
-  MA_DISPATCH2(dt_g, dt_m, k_rowsumsq_momentum, dim3(blocks), dim3(256), 0, s, a);
+  // chunks of 512 columns per row, rounded up to the kernel's batch width
+  const int cpr = (a.C + 511) / 512;
+  if (cpr <= 1) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 1, dim3(blocks), dim3(256), 0, s, a);
+  else if (cpr <= 2) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 2, dim3(blocks), dim3(256), 0, s, a);
+  else if (cpr <= 4) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 4, dim3(blocks), dim3(256), 0, s, a);
+  else MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 8, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+#define MA_DISPATCH3C(d1, d2, d3, KER, C4, ...)                                            \
+  do {                                                                                     \
+    if ((d3) == DT_BF16) MA_DISPATCH2C3(d1, d2, DT_BF16, KER, C4, __VA_ARGS__);            \
+    else MA_DISPATCH2C3(d1, d2, DT_F32, KER, C4, __VA_ARGS__);                             \
+  } while (0)
+#define MA_DISPATCH2C3(d1, d2, D3, KER, C4, ...)                                                          \
+  do {                                                                                                    \
+    if ((d1) == DT_BF16 && (d2) == DT_BF16) hipLaunchKernelGGL((KER<DT_BF16, DT_BF16, D3, C4>), __VA_ARGS__); \
+    else if ((d1) == DT_BF16) hipLaunchKernelGGL((KER<DT_BF16, DT_F32, D3, C4>), __VA_ARGS__);            \
+    else if ((d2) == DT_BF16) hipLaunchKernelGGL((KER<DT_F32, DT_BF16, D3, C4>), __VA_ARGS__);            \
+    else hipLaunchKernelGGL((KER<DT_F32, DT_F32, D3, C4>), __VA_ARGS__);                                   \
+  } while (0)
+
+hipError_t launch_pre_rows(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s) {
+  if (!a.vec || !a.xd || a.R > a.r_ext || a.C > a.c_ext || a.c_ext > kPreRowsMaxCols || (a.ld_d % 8) != 0)
+    return hipErrorInvalidValue;
+  const int blocks = a.count * ((a.r_ext + 3) / 4);
+  if (blocks <= 0) return hipSuccess;
+  const int ch = (a.c_ext + 511) / 512;
+  if (ch <= 1) MA_DISPATCH3C(dt_g, dt_m, dt_x, k_pre_rows, 1, dim3(blocks), dim3(256), 0, s, a);
+  else if (ch <= 2) MA_DISPATCH3C(dt_g, dt_m, dt_x, k_pre_rows, 2, dim3(blocks), dim3(256), 0, s, a);
+  else if (ch <= 4) MA_DISPATCH3C(dt_g, dt_m, dt_x, k_pre_rows, 4, dim3(blocks), dim3(256), 0, s, a);
+  else MA_DISPATCH3C(dt_g, dt_m, dt_x, k_pre_rows, 8, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,8 @@ struct ElemArgs {
   float c_lr, c_wd;
   int32_t cautious, decay;
   float norm_eps, eq_eps;
-  int32_t finalize_mode;     // 0: Frobenius only, 1: MuonEq pre, 2: MuonEq post
+  int32_t finalize_mode;     // 0: Frobenius only, 1: MuonEq pre, 2: MuonEq post, 3: row RMS,
+                             // 4: MuonEq pre, Frobenius factor only (into rowf[0])
   int32_t vec;               // C % 8 == 0 and every matrix pointer 16-byte aligned
   int32_t pure_copy;         // k_pre: X0 = G (no momentum; M untouched)
   float* part;               // k_post: per-block (sum (W'-W)^2, sum W^2), 2 floats per block, or null
@@ -40,6 +41,12 @@ hipError_t launch_rowsumsq_momentum(int dt_g, int dt_m, const ElemArgs& a, hipSt
 hipError_t launch_rowsumsq_buffer(int dt_x, const ElemArgs& a, hipStream_t s);
 hipError_t launch_finalize(const ElemArgs& a, hipStream_t s);
 hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s);
+// k_pre_rows (momentum, row sums and the row-scaled X0 in one pass; the
+// Frobenius factor left to the iteration) for matrices whose iteration layout
+// is the parameter's; launch_pre_rows fails with hipErrorInvalidValue unless
+// a.vec, a.xd is set, R <= r_ext, C <= c_ext <= kPreRowsMaxCols and ld_d % 8 == 0
+constexpr int kPreRowsMaxCols = 4096;
+hipError_t launch_pre_rows(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s);
 hipError_t launch_post(int dt_p, int dt_x, const ElemArgs& a, hipStream_t s);
 // blocks per matrix of the launch_post call for `a` (the partial sums it writes)
 int post_blocks_per_mat(const ElemArgs& a);

@@ -231,6 +231,19 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
         asm volatile("" ::: "memory");
       }
   }
+  if constexpr (EPI != EPI_POLY) {
+    if (G.scale) {
+      // X = s Y with Y in the operand buffers: A = s^2 Y Y^T, X' = s (a Y + B Y)
+      float sc = G.scale[(int64_t)mat * G.scale_stride];
+      if constexpr (EPI == EPI_GRAM) sc = sc * sc;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
+    }
+  }
   if constexpr (EPI == EPI_POLY && E_DONE) {
     // the main loop accumulated A A + (b/c) A
 #pragma unroll

@@ -36,6 +36,11 @@ struct NsGroup {
   int32_t p_upper;    // AXPY with qt: P holds only its upper triangle (B
                       // symmetric); blocks left of the diagonal are read
                       // transposed from those above it
+  // per-matrix factor s of the operand X (matrix k's at scale[k*scale_stride]),
+  // or null: the output is multiplied by s^2 (GRAM, A of s X) or s (AXPY,
+  // X' of s X given B of s X)
+  const float* scale;
+  int64_t scale_stride;
 };
 
 // Scheduling: the hardware deals consecutive workgroups round-robin to the 8

@@ -56,14 +56,16 @@ def elem_bytes(dt):
     return 2 if dt == "bf16" else 4
 
 
-def work_model(wl, ns_steps):
-    """Algorithmic work per launch of each kernel kind (per step for the rest)."""
+def work_model(wl, ns_steps, row_pass=None):
+    """Algorithmic work per launch of each kernel kind (per step for the rest).
+    row_pass[i]: group i reads G and M once (momentum, row sums and X0 in one
+    pass, counted under "pre"); otherwise the row sums read them first."""
     ex = elem_bytes(wl.ns_precision)
     ep, eg, em = elem_bytes(wl.param_dtype), elem_bytes(wl.grad_dtype), elem_bytes(wl.mom_dtype)
     gram = poly = axpy = 0.0
     gram_b = poly_b = axpy_b = 0.0
     pre = rown = post = 0.0
-    for g in wl.muon_groups:
+    for gi, g in enumerate(wl.muon_groups):
         m, n = min(g.rows, g.cols), max(g.rows, g.cols)
         gram += g.count * m * m * n          # A = X X^T, symmetric: m^2 n
         poly += g.count * m * m * m          # A A, symmetric: m^3
@@ -74,7 +76,8 @@ def work_model(wl, ns_steps):
         poly_b += g.count * (2.0 * m * m) * ex
         axpy_b += g.count * (m * m + 2.0 * m * n) * ex
         e = g.rows * g.cols * g.count
-        rown += e * (eg + em)                # read G, M
+        if not (row_pass and row_pass[gi]):
+            rown += e * (eg + em)            # read G, M
         pre += e * (eg + 2 * em + ex)        # read G, M; write M, X0
         post += e * (2 * ep + ex)            # read W, U; write W
     adam = 28.0 * wl.adamw_numel
@@ -193,7 +196,7 @@ def main():
 
     # per-kernel durations from the events recorded around each launch
     import ctypes as C
-    model = work_model(wl, T)
+    model = work_model(wl, T, [M.muon_row_pass(groups, hp, i) for i in range(len(groups))])
     kernels = {}
     if profile:
         for kind, name in enumerate(L.KERNEL_KINDS):

@@ -139,6 +139,10 @@ size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
  *   m1 = beta*M + G (fp32); M <- m1 rounded to mom_dtype (RNE)
  *   Mt = G + beta*m1 if nesterov else m1                      (fp32)
  *   optional MuonEq PRE; X0 = Mt / (||Mt||_F + norm_eps)
+ *     (with MuonEq PRE and T >= 1, groups for which ma_muon_row_pass is 1
+ *     store the row-scaled Mt rounded to the iteration's precision and apply
+ *     1 / (||.||_F + norm_eps) in the first Gram product and update: the same
+ *     X0 with one rounding at a different point)
  *   if R > C the iteration runs on X0^T (layout, no extra copy)
  *   T quintic steps with the caller's coefficient table
  *   optional MuonEq POST; U = final iterate in W's layout
@@ -168,6 +172,17 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
  * The update itself is identical to ma_muon_step's. */
 int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                        void* workspace, size_t workspace_bytes, float* stats, void* stream);
+
+/* Whether ma_muon_step treats group `group` in one pass over G and M: the
+ * momentum update, MuonEq PRE's row sums and the row-scaled X0 together, the
+ * Frobenius factor of "Chapter 4: The MuonAdamW Optimizer" (section "Polar
+ * Express: Newton-Schulz Orthogonalization") then applied by the first
+ * Newton-Schulz products. That is the case for MuonEq PRE with T >= 1, a bf16
+ * iteration, rows <= cols, cols a multiple of 8 and at most 4096 (after
+ * padding to 256), 16-byte aligned buffers, unless the environment sets
+ * MA_PRE_ROWS=0. Returns 1 or 0, or a negative MA_ERR_* for invalid
+ * arguments (as ma_muon_workspace_size validates them). Host-only. */
+int ma_muon_row_pass(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, int32_t group);
 
 /* Where matrix `index` of group `group` keeps the result of its Newton-Schulz
  * iteration inside a workspace after ma_muon_step (for inspection; valid

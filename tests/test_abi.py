@@ -77,6 +77,31 @@ def test_workspace_size_lower_bound():
     assert L.lib().ma_muon_workspace_size((L.MuonGroupC * 1)(g), 1, C.byref(h32)) >= 2 * n2 - (1 << 20)
 
 
+@pytest.mark.parametrize("rows,cols,kw,base,expect", [
+    (1024, 1024, {}, BASE, 1),
+    (1024, 4096, {}, BASE, 1),
+    (20, 1000, {}, BASE, 1),                       # 1000 columns pad to 1024
+    (4096, 1024, {}, BASE, 0),                     # tall: the iteration runs on X^T
+    (1024, 4104, {}, BASE, 0),                     # 4104 pads to 4352 > 4096
+    (100, 300, {}, BASE, 0),                       # cols % 8 != 0: no vector path
+    (1024, 1024, {}, BASE + 8, 0),                 # 8-byte aligned buffers
+    (1024, 1024, dict(equilibrate="off"), BASE, 0),
+    (1024, 1024, dict(equilibrate="post"), BASE, 0),
+    (1024, 1024, dict(ns_steps=0), BASE, 0),
+    (1024, 1024, dict(ns_precision="f32"), BASE, 0),
+])
+def test_row_pass_predicate(rows, cols, kw, base, expect):
+    """Which groups ma_muon_step reads in one pass (host-only query)."""
+    if os.environ.get("MA_PRE_ROWS") == "0" or os.environ.get("MA_NS_QT") == "0":
+        pytest.skip("one-pass form switched off in this environment")
+    g, k = group(rows=rows, cols=cols, count=2, base=base)
+    args = dict(equilibrate="pre", ns_steps=5)
+    args.update(kw)
+    h, t = hp(**args)
+    assert L.lib().ma_muon_row_pass((L.MuonGroupC * 1)(g), 1, C.byref(h), 0) == expect
+    assert L.lib().ma_muon_row_pass((L.MuonGroupC * 1)(g), 1, C.byref(h), 1) == L.MA_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("mut,code", [
     (lambda g, h: setattr(h, "ns_steps", 17), L.MA_ERR_INVALID_ARG),
     (lambda g, h: setattr(h, "ns_steps", -1), L.MA_ERR_INVALID_ARG),

@@ -211,6 +211,36 @@ def test_ragged_groups(eq, cautious, wd, dts):
     _check_step(groups_np, dev, mgs, ws, hp, dts)
 
 
+@pytest.mark.parametrize("steps", [0, 5])
+@pytest.mark.parametrize("dts", [("f32", "f32", "f32"), ("bf16", "bf16", "bf16"), ("bf16", "bf16", "f32")])
+def test_row_norms_of_long_rows(steps, dts):
+    """MuonEq row factors for rows of one to seventeen 512-column chunks:
+    1024 columns (two chunks, four rows read together), 1536 (three of a
+    four-chunk batch), 4608 and 8200 (eight-chunk batches, the last partial),
+    row counts that leave a wave's four rows part empty, and a tall matrix
+    whose rows are 1000 long. With no Newton-Schulz step the update is the
+    row-scaled look-ahead itself, so a row sum that lost a chunk shows at the
+    fp32 tolerance."""
+    rng = np.random.default_rng(91)
+    groups_np = []
+    for R, C, n in [(20, 1024, 2), (7, 1536, 1), (5, 4608, 1), (3, 8200, 1), (1100, 1000, 1)]:
+        W = (rng.standard_normal((n, R, C)) * 0.02).astype(np.float32)
+        G = (rng.standard_normal((n, R, C)) * 1e-3).astype(np.float32)
+        Mo = (rng.standard_normal((n, R, C)) * 3e-3).astype(np.float32)
+        # one row far larger than the rest, one near zero
+        G[:, 0, :] *= 50.0
+        G[:, -1, :] *= 1e-3
+        Mo[:, -1, :] *= 1e-3
+        W, G, Mo = [O.round_to_bf16(a) if d == "bf16" else a for a, d in zip((W, G, Mo), dts)]
+        groups_np.append((W, G, Mo))
+    prec = "f32" if dts[0] == "f32" else "bf16"
+    hp = _hp(equilibrate="pre", cautious=True, weight_decay=0.01, ns_precision=prec, ns_steps=steps,
+             coeffs=KJ)
+    say("long rows", steps, dts)
+    dev, mgs, ws = _run_step(groups_np, hp, dts)
+    _check_step(groups_np, dev, mgs, ws, hp, dts)
+
+
 @pytest.mark.parametrize("scale", ["none", "sqrt_max1_r_over_c", "moonshot", "sqrt_max"])
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 def test_lr_scales(scale, prec):
