@@ -12,7 +12,8 @@
 //
 // 28 bytes of HBM traffic per element (p, g, m, v read; p, m, v written).
 // Each block streams 4096 consecutive elements of one segment with 16-byte
-// loads (all loads of a thread issued before its arithmetic); a table of
+// non-temporal loads and stores (all loads of a thread issued before its
+// arithmetic; the state is touched once per step); a table of
 // segments in the kernel arguments lets one launch cover every buffer, the
 // multi-tensor ("fused"/"foreach") form the pages mention.
 #include "adamw.hpp"
@@ -45,10 +46,10 @@ __global__ void __launch_bounds__(256) k_adamw(const AdamArgs a) {
       const int64_t i = e0 + (int64_t)(u * 256 + tid) * 4;
       full[u] = i + 4 <= S.n;
       if (full[u]) {
-        p[u] = *reinterpret_cast<const float4*>(S.p + i);
-        g[u] = *reinterpret_cast<const float4*>(S.g + i);
-        m[u] = *reinterpret_cast<const float4*>(S.m + i);
-        v[u] = *reinterpret_cast<const float4*>(S.v + i);
+        p[u] = ld16f<true>(S.p + i);
+        g[u] = ld16f<true>(S.g + i);
+        m[u] = ld16f<true>(S.m + i);
+        v[u] = ld16f<true>(S.v + i);
       }
     }
 #pragma unroll
@@ -59,9 +60,9 @@ __global__ void __launch_bounds__(256) k_adamw(const AdamArgs a) {
         adamw_elem(p[u].y, g[u].y, m[u].y, v[u].y, S);
         adamw_elem(p[u].z, g[u].z, m[u].z, v[u].z, S);
         adamw_elem(p[u].w, g[u].w, m[u].w, v[u].w, S);
-        *reinterpret_cast<float4*>(S.p + i) = p[u];
-        *reinterpret_cast<float4*>(S.m + i) = m[u];
-        *reinterpret_cast<float4*>(S.v + i) = v[u];
+        st16f<true>(S.p + i, p[u]);
+        st16f<true>(S.m + i, m[u]);
+        st16f<true>(S.v + i, v[u]);
       } else {
         for (int64_t j = i; j < S.n && j < i + 4; ++j) {
           float pp = S.p[j], mm = S.m[j], vv = S.v[j];

@@ -44,12 +44,52 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
+// 16-byte loads and stores, optionally non-temporal (`nt`): for data a step
+// touches once (gradients, optimizer state, parameters, the final update), so
+// that it neither displaces the iteration's operands in the caches nor leaves
+// dirty lines for the next kernel's traffic to wait behind.
+typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (NT) {
+    const u32x4_nt_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, const uint4& x) {
+  if constexpr (NT) {
+    const u32x4_nt_t y = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(y, reinterpret_cast<u32x4_nt_t*>(p));
+  } else {
+    *reinterpret_cast<uint4*>(p) = x;
+  }
+}
+template <bool NT>
+__device__ __forceinline__ float4 ld16f(const void* p) {
+  const uint4 u = ld16<NT>(p);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+template <bool NT>
+__device__ __forceinline__ void st16f(void* p, const float4& x) {
+  st16<NT>(p, make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)));
+}
+
+// Non-temporal access in the Muon elementwise kernels (build with -DMA_NT=0
+// to compare against cached access).
+#ifndef MA_NT
+#define MA_NT 1
+#endif
+constexpr bool kNT = MA_NT != 0;
+
 // load / store n consecutive elements of storage type DT as fp32 (n = 8: one
 // 16-byte vector for bf16, two for fp32). Pointers must be 16-byte aligned.
-template <int DT>
+template <int DT, bool NT = false>
 __device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
   if constexpr (DT == DT_BF16) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint4 u = ld16<NT>(p);
     uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -57,14 +97,14 @@ __device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    float4 a = reinterpret_cast<const float4*>(p)[0];
-    float4 b = reinterpret_cast<const float4*>(p)[1];
+    float4 a = ld16f<NT>(p);
+    float4 b = ld16f<NT>(reinterpret_cast<const float4*>(p) + 1);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
 }
 
-template <int DT>
+template <int DT, bool NT = false>
 __device__ __forceinline__ void store8(void* p, const float (&v)[8]) {
   if constexpr (DT == DT_BF16) {
     uint4 u;
@@ -72,10 +112,10 @@ __device__ __forceinline__ void store8(void* p, const float (&v)[8]) {
     u.y = pack_bf16x2(v[2], v[3]);
     u.z = pack_bf16x2(v[4], v[5]);
     u.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p) = u;
+    st16<NT>(p, u);
   } else {
-    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    st16f<NT>(p, make_float4(v[0], v[1], v[2], v[3]));
+    st16f<NT>(reinterpret_cast<float4*>(p) + 1, make_float4(v[4], v[5], v[6], v[7]));
   }
 }
 

@@ -45,9 +45,9 @@ __global__ void __launch_bounds__(256) k_lion(const LionArgs a) {
       const int64_t i = e0 + (int64_t)(u * 256 + tid) * 4;
       full[u] = i + 4 <= S.n;
       if (full[u]) {
-        p[u] = *reinterpret_cast<const float4*>(S.p + i);
-        g[u] = *reinterpret_cast<const float4*>(S.g + i);
-        m[u] = *reinterpret_cast<const float4*>(S.m + i);
+        p[u] = ld16f<true>(S.p + i);
+        g[u] = ld16f<true>(S.g + i);
+        m[u] = ld16f<true>(S.m + i);
       }
     }
 #pragma unroll
@@ -58,8 +58,8 @@ __global__ void __launch_bounds__(256) k_lion(const LionArgs a) {
         lion_elem(p[u].y, g[u].y, m[u].y, S);
         lion_elem(p[u].z, g[u].z, m[u].z, S);
         lion_elem(p[u].w, g[u].w, m[u].w, S);
-        *reinterpret_cast<float4*>(S.p + i) = p[u];
-        *reinterpret_cast<float4*>(S.m + i) = m[u];
+        st16f<true>(S.p + i, p[u]);
+        st16f<true>(S.m + i, m[u]);
       } else {
         for (int64_t j = i; j < S.n && j < i + 4; ++j) {
           float pp = S.p[j], mm = S.m[j];

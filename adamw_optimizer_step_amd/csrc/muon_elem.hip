@@ -50,10 +50,10 @@ template <int DT>
 struct Raw8 {
   uint4 w[DT == DT_BF16 ? 1 : 2];
 };
-template <int DT>
+template <int DT, bool NT = false>
 __device__ __forceinline__ void raw_load(const void* p, Raw8<DT>& r) {
 #pragma unroll
-  for (int i = 0; i < (DT == DT_BF16 ? 1 : 2); ++i) r.w[i] = reinterpret_cast<const uint4*>(p)[i];
+  for (int i = 0; i < (DT == DT_BF16 ? 1 : 2); ++i) r.w[i] = ld16<NT>(reinterpret_cast<const uint4*>(p) + i);
 }
 template <int DT>
 __device__ __forceinline__ float raw_at(const Raw8<DT>& r, int e) {
@@ -241,15 +241,15 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
         for (int e = 0; e < 8; ++e) x[e] = c + e < a.C ? load1<DTG>(gp, off + e) : 0.0f;
       } else if (vec) {
         float g[8], m[8], m1[8];
-        load8<DTG>(eptr<DTG>(gp, off), g);
-        load8<DTM>(eptr<DTM>(static_cast<const void*>(mp), off), m);
+        load8<DTG, kNT>(eptr<DTG>(gp, off), g);
+        load8<DTM, kNT>(eptr<DTM>(static_cast<const void*>(mp), off), m);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float mt;
           momentum1(g[e], m[e], a.beta, a.nesterov, m1[e], mt);
           x[e] = __fmul_rn(mt, f);
         }
-        store8<DTM>(eptr<DTM>(mp, off), m1);
+        store8<DTM, kNT>(eptr<DTM>(mp, off), m1);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -334,8 +334,8 @@ __global__ void __launch_bounds__(256) k_pre_rows(const ElemArgs a) {
     const int c = u * 512 + lane * 8;
     ok[u] = c < a.C;
     const int64_t off = ok[u] ? (int64_t)r * a.C + c : 0;
-    raw_load<DTG>(eptr<DTG>(gp, off), g[u]);
-    raw_load<DTM>(eptr<DTM>(static_cast<const void*>(mp), off), m[u]);
+    raw_load<DTG, kNT>(eptr<DTG>(gp, off), g[u]);
+    raw_load<DTM, kNT>(eptr<DTM>(static_cast<const void*>(mp), off), m[u]);
   }
   float mt[CH][8];
   float acc = 0.0f;
@@ -348,7 +348,7 @@ __global__ void __launch_bounds__(256) k_pre_rows(const ElemArgs a) {
       const float t = __builtin_fmaf(mt[u][e], mt[u][e], acc);
       acc = ok[u] ? t : acc;
     }
-    if (ok[u]) store8<DTM>(eptr<DTM>(mp, (int64_t)r * a.C + u * 512 + lane * 8), m1);
+    if (ok[u]) store8<DTM, kNT>(eptr<DTM>(mp, (int64_t)r * a.C + u * 512 + lane * 8), m1);
   }
   const float n2 = wave_sum(acc);
   if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = n2;
@@ -425,8 +425,8 @@ __device__ __forceinline__ void post_vec_body(const ElemArgs& a, int blocks_per_
       rr[v] = q / cpr;
       cc[v] = (q - rr[v] * cpr) * 8u;
       if (q < nch) {
-        load8<DTP>(eptr<DTP>(static_cast<const void*>(wp), (int64_t)rr[v] * a.C + cc[v]), w[v]);
-        load8<DTX>(eptr<DTX>(xd, (int64_t)rr[v] * a.ld_d + cc[v]), u[v]);
+        load8<DTP, kNT>(eptr<DTP>(static_cast<const void*>(wp), (int64_t)rr[v] * a.C + cc[v]), w[v]);
+        load8<DTX, kNT>(eptr<DTX>(xd, (int64_t)rr[v] * a.ld_d + cc[v]), u[v]);
       }
     }
 #pragma unroll
@@ -439,7 +439,7 @@ __device__ __forceinline__ void post_vec_body(const ElemArgs& a, int blocks_per_
           w[v][e] = post_elem(w0, u[v][e], f, rowf != nullptr, a);
           if constexpr (STATS) update_sums<DTP>(w0, w[v][e], sd, sw);
         }
-        store8<DTP>(eptr<DTP>(wp, (int64_t)rr[v] * a.C + cc[v]), w[v]);
+        store8<DTP, kNT>(eptr<DTP>(wp, (int64_t)rr[v] * a.C + cc[v]), w[v]);
       }
     }
   }
