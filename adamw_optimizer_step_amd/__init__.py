@@ -6,7 +6,8 @@ binding. Build the library with ``python -m adamw_optimizer_step_amd.build``.
 """
 from .api import (  # noqa: F401
     KELLER_JORDAN, MuonGroup, MuonHParams, adamw_step, bf16_round, lion_step, momentum_stage,
-    muon_row_pass, muon_step, muon_workspace_size, muon_workspace_update, newton_schulz, update_stage,
+    muon_row_pass, muon_step, muon_workspace_size, muon_workspace_update, newton_schulz, optimizer_step,
+    update_stage,
 )
 from ._lib import MuonAdamWError, lib  # noqa: F401
 from .coefficients import keller_jordan, polar_express  # noqa: F401
@@ -18,5 +19,5 @@ POLAR_EXPRESS = tuple(polar_express(5, lower=1e-3, safety=1.01))
 
 __all__ = [
     "KELLER_JORDAN", "POLAR_EXPRESS", "keller_jordan", "polar_express", "MuonGroup", "MuonHParams", "MuonAdamWError", "adamw_step", "lion_step", "muon_step",
-    "muon_row_pass", "muon_workspace_size", "muon_workspace_update", "lib",
+    "muon_row_pass", "muon_workspace_size", "muon_workspace_update", "optimizer_step", "lib",
 ]

@@ -187,9 +187,12 @@ def muon_workspace_update(groups: Sequence[MuonGroup], hp: MuonHParams, workspac
     return flat.view(g.rows, ld.value)[:, : g.cols]
 
 
-def adamw_step(segments: Sequence[dict], stream=None) -> None:
+def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] = None) -> None:
     """One AdamW step. Each segment: param, grad, exp_avg, exp_avg_sq (fp32
-    tensors, contiguous), lr, beta1, beta2, eps, weight_decay, step (1-based)."""
+    tensors, contiguous), lr, beta1, beta2, eps, weight_decay, step (1-based).
+    With ``workgroups``, the same update by that many persistent workgroups
+    with a small register footprint (``ma_adamw_step_background``), for
+    running beside the Newton-Schulz GEMMs on another stream."""
     if not segments:
         return
     arr = (L.AdamWSegmentC * len(segments))()
@@ -204,7 +207,44 @@ def adamw_step(segments: Sequence[dict], stream=None) -> None:
                                  grad_dtype=_dt(g), lr=s["lr"], beta1=s.get("beta1", 0.9),
                                  beta2=s.get("beta2", 0.95), eps=s.get("eps", 1e-8),
                                  weight_decay=s.get("weight_decay", 0.0), step=int(s["step"]))
-    L.check(L.lib().ma_adamw_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
+    if workgroups is None:
+        L.check(L.lib().ma_adamw_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
+    else:
+        L.check(L.lib().ma_adamw_step_background(arr, len(segments), int(workgroups),
+                                                 C.c_void_p(_stream(dev, stream))))
+
+
+_SIDE = {}
+
+
+def optimizer_step(groups: Sequence[MuonGroup], hp: MuonHParams, adamw_segments: Sequence[dict],
+                   workspace: Optional[torch.Tensor] = None, overlap: bool = True,
+                   background_workgroups: int = 256) -> torch.Tensor:
+    """One MuonAdamW step: ``muon_step`` over ``groups`` and ``adamw_step``
+    over ``adamw_segments`` (disjoint buffers), both ordered after the work
+    already on the current stream, with everything done once the current
+    stream reaches the end of the call. With ``overlap``, AdamW runs on a
+    second stream (default priority) by ``background_workgroups`` lean
+    workgroups while the Muon step runs on the current one, so that the
+    HBM-bound update shares the GPU with the MFMA-bound iteration; the
+    results are identical either way. Capturable in a HIP graph. Returns the
+    Muon workspace."""
+    if not adamw_segments:
+        return muon_step(groups, hp, workspace=workspace)
+    dev = adamw_segments[0]["param"].device
+    if not overlap:
+        ws = muon_step(groups, hp, workspace=workspace)
+        adamw_step(adamw_segments)
+        return ws
+    cur = torch.cuda.current_stream(dev)
+    side = _SIDE.get(dev)
+    if side is None:
+        side = _SIDE[dev] = torch.cuda.Stream(device=dev)
+    side.wait_stream(cur)
+    adamw_step(adamw_segments, stream=side, workgroups=background_workgroups)
+    ws = muon_step(groups, hp, workspace=workspace)
+    cur.wait_stream(side)
+    return ws
 
 
 def lion_step(segments: Sequence[dict], stream=None) -> None:

@@ -22,6 +22,7 @@ struct AdamSeg {
 struct AdamArgs {
   int32_t nseg;
   int32_t total_blocks;
+  int32_t lean_blocks;   // > 0: k_adamw_lean with this many workgroups (at most)
   AdamSeg s[kMaxAdamSegs];
 };
 

@@ -642,7 +642,8 @@ int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups, cons
   return MA_OK;
 }
 
-int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
+namespace {
+int adamw_impl(const ma_adamw_segment* segs, int32_t n, int32_t lean_blocks, void* stream) {
   if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
   std::vector<Range> rs;
   for (int i = 0; i < n; ++i) {
@@ -679,9 +680,11 @@ int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
       err = launch_adamw(A, s);
     }
     A = AdamArgs{};
+    A.lean_blocks = lean_blocks;
     blocks = 0;
     return err == hipSuccess ? MA_OK : hip_fail(err, "AdamW launch");
   };
+  A.lean_blocks = lean_blocks;
   for (int i = 0; i < n; ++i) {
     const ma_adamw_segment& S = segs[i];
     if (S.n == 0) continue;
@@ -711,6 +714,16 @@ int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
     blocks += nb;
   }
   return flush();
+}
+}  // namespace
+
+int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
+  return adamw_impl(segs, n, 0, stream);
+}
+
+int ma_adamw_step_background(const ma_adamw_segment* segs, int32_t n, int32_t workgroups, void* stream) {
+  if (workgroups < 1) return fail(MA_ERR_INVALID_ARG, "workgroups must be >= 1");
+  return adamw_impl(segs, n, workgroups, stream);
 }
 
 int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {

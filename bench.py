@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (one captured step replayed --steps times)")
     ap.add_argument("--no-lion", action="store_true", help="skip the separate Lion step timing")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run AdamW after the Muon step on the same stream instead of beside it on a second one")
+    ap.add_argument("--adamw-workgroups", type=int, default=256,
+                    help="workgroups of the AdamW update when it runs beside the Muon step")
     ap.add_argument("--no-practical", action="store_true", help="skip the practical-peak calibration kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed steps, run 3 plain device copies of MIB MiB (read MIB, write MIB) "
@@ -125,11 +129,11 @@ def main():
                          lr=s.lr, beta1=s.beta1, beta2=s.beta2, eps=s.eps, weight_decay=s.weight_decay))
 
     def step(i):
-        M.muon_step(groups, hp, workspace=ws)
-        if segs:
-            for s in segs:
-                s["step"] = wl.adamw_step + i
-            M.adamw_step(segs)
+        for s in segs:
+            s["step"] = wl.adamw_step + i
+        # AdamW on a second stream beside the Muon step unless --no-overlap
+        M.optimizer_step(groups, hp, segs, workspace=ws, overlap=not args.no_overlap,
+                         background_workgroups=args.adamw_workgroups)
 
     for i in range(args.warmup):
         step(i)
@@ -272,6 +276,8 @@ def main():
                    "muon_matrices": sum(g.count for g in wl.muon_groups),
                    "muon_elements": wl.muon_numel, "adamw_elements": wl.adamw_numel,
                    "parallelism": "single GPU",
+                   "streams": ("AdamW on a second stream beside the Muon step" if (data["adamw"] and not args.no_overlap)
+                               else "one stream"),
                    "timing": ("HIP-graph replay of one captured step" if ms_graph is not None and ms == ms_graph
                               else "eager launches"),
                    "ms_per_step_eager": round(ms_eager, 4),

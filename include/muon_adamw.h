@@ -222,6 +222,16 @@ typedef struct {
  * `segments` is a HOST array. */
 int ma_adamw_step(const ma_adamw_segment* segments, int32_t n_segments, void* stream);
 
+/* ma_adamw_step with identical results, run by at most `workgroups`
+ * persistent workgroups that each keep one 16-byte chunk per buffer in
+ * flight per thread: a register footprint small enough for a workgroup to
+ * share a CU with a Newton-Schulz GEMM workgroup. For issuing the AdamW part
+ * of a step on a second stream while ma_muon_step runs on another (the two
+ * touch disjoint buffers); alone it is slower than ma_adamw_step. workgroups
+ * >= 1 (MA_ERR_INVALID_ARG otherwise); 256, one per CU, suits MI355X. */
+int ma_adamw_step_background(const ma_adamw_segment* segments, int32_t n_segments, int32_t workgroups,
+                             void* stream);
+
 /* One flat Lion buffer. param, grad, exp_avg (the momentum, Lion's only
  * state): DEVICE pointers to n elements each, fp32 (param_dtype and
  * grad_dtype must be MA_F32), 4-byte aligned. */

@@ -191,6 +191,16 @@ def test_adamw_rejects_bad_arguments(kw, code):
     assert L.lib().ma_adamw_step(arr, 1, None) == code
 
 
+def test_adamw_background_validates_workgroups():
+    seg = L.AdamWSegmentC(param=BASE, grad=BASE + (1 << 24), exp_avg=BASE + (2 << 24), exp_avg_sq=BASE + (3 << 24),
+                          n=1000, param_dtype=0, grad_dtype=0, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                          weight_decay=0.0, step=1)
+    arr = (L.AdamWSegmentC * 1)(seg)
+    for wg in (0, -1):
+        assert L.lib().ma_adamw_step_background(arr, 1, wg, None) == L.MA_ERR_INVALID_ARG
+    assert L.lib().ma_adamw_step_background(None, 0, 256, None) == 0
+
+
 def test_adamw_zero_segments_is_noop():
     assert L.lib().ma_adamw_step(None, 0, None) == L.MA_OK
     arr = (L.AdamWSegmentC * 1)(seg(n=0, param=None, grad=None, exp_avg=None, exp_avg_sq=None))

@@ -4,7 +4,9 @@ replay, the same bits as the same step launched eagerly.
 The library launches only kernels on the caller's stream (no allocation, no
 memset, no host synchronisation), so a whole optimizer step can be captured.
 Each replay is checked against an eager step from the same state, with the
-program's own eager work and synchronisations between replays.
+program's own eager work and synchronisations between replays. The captured
+step runs AdamW either after the Muon step or on a second stream beside it
+(forked and joined inside the capture); the eager reference runs them in turn.
 """
 import numpy as np
 import pytest
@@ -35,7 +37,7 @@ def _to_dev(muon, ad):
     return [[t.to(DEV).contiguous() for t in grp] for grp in muon], [t.to(DEV).contiguous() for t in ad]
 
 
-def _stepper(M, muon, ad, ws):
+def _stepper(M, muon, ad, ws, overlap=False):
     groups = [M.MuonGroup(W, G, Mo) for W, G, Mo in muon]
     hp = M.MuonHParams(lr=0.02, momentum=0.95, weight_decay=0.01, nesterov=True, ns_steps=5,
                        coeffs=M.KELLER_JORDAN, cautious=True, equilibrate="pre", ns_precision="bf16")
@@ -43,8 +45,12 @@ def _stepper(M, muon, ad, ws):
                 beta2=0.95, eps=1e-8, weight_decay=0.1)]
 
     def step():
-        M.muon_step(groups, hp, workspace=ws)
-        M.adamw_step(seg)
+        if overlap:
+            # AdamW forked onto a second stream and joined: two branches in the graph
+            M.optimizer_step(groups, hp, seg, workspace=ws, overlap=True)
+        else:
+            M.muon_step(groups, hp, workspace=ws)
+            M.adamw_step(seg)
     return groups, hp, step
 
 
@@ -53,7 +59,8 @@ def _snapshot(muon, ad):
            [t.detach().cpu().view(torch.int32).numpy().copy() for t in (ad[0], ad[2], ad[3])]
 
 
-def test_graph_replays_match_eager_steps():
+@pytest.mark.parametrize("overlap", [False, True])
+def test_graph_replays_match_eager_steps(overlap):
     need_gpu()
     import adamw_optimizer_step_amd as M
     init_m, init_a = _state(3)
@@ -65,7 +72,7 @@ def test_graph_replays_match_eager_steps():
     # graph copy: warm up on the capture stream, reset the state, capture
     gm, ga = _to_dev(init_m, init_a)
     gws = torch.empty_like(ews)
-    _, _, gstep = _stepper(M, gm, ga, gws)
+    _, _, gstep = _stepper(M, gm, ga, gws, overlap=overlap)
     cap = torch.cuda.Stream(DEV)
     cap.wait_stream(torch.cuda.current_stream(DEV))
     with torch.cuda.stream(cap):

@@ -69,7 +69,10 @@ def _adamw_case(sizes, seed, step, wd, offset=0):
     ((50000, 4096), 3, 0.01, 1),      # element offset 1: unaligned buffers, scalar path
     ((2,) * 30, 2, 0.1, 0),           # more segments than one launch holds
 ])
-def test_adamw_bit_exact(sizes, step, wd, offset):
+@pytest.mark.parametrize("workgroups", [None, 256, 3])
+def test_adamw_bit_exact(sizes, step, wd, offset, workgroups):
+    """ma_adamw_step, and ma_adamw_step_background with one workgroup per CU
+    and with 3 workgroups striding over every block of every segment."""
     import adamw_optimizer_step_amd as M
     segs_np = _adamw_case(sizes, seed=len(sizes) * 31 + step, step=step, wd=wd)
     segs, keep = [], []
@@ -81,8 +84,8 @@ def test_adamw_bit_exact(sizes, step, wd, offset):
             keep.append(buf)
             ts.append(buf[offset:])
         segs.append(dict(param=ts[0], grad=ts[1], exp_avg=ts[2], exp_avg_sq=ts[3], step=step, **hp))
-    say("adamw", sizes, step, wd, offset)
-    M.adamw_step(segs)
+    say("adamw", sizes, step, wd, offset, workgroups)
+    M.adamw_step(segs, workgroups=workgroups)
     torch.cuda.synchronize()
     for (p, g, m, v, hp), s in zip(segs_np, segs):
         ep, em, ev = O.adamw_step(p, g, m, v, step, **hp)
