@@ -74,6 +74,9 @@ EXPORTS = {
                                            C.POINTER(C.c_int32)]),
     "ma_adamw_step": (C.c_int, [C.POINTER(AdamWSegmentC), C.c_int32, C.c_void_p]),
     "ma_adamw_step_background": (C.c_int, [C.POINTER(AdamWSegmentC), C.c_int32, C.c_int32, C.c_void_p]),
+    "ma_muon_adamw_step": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
+                                     C.c_size_t, C.POINTER(AdamWSegmentC), C.c_int32, C.c_int32, C.c_void_p,
+                                     C.c_void_p]),
     "ma_lion_step": (C.c_int, [C.POINTER(LionSegmentC), C.c_int32, C.c_void_p]),
     "ma_status_string": (C.c_char_p, [C.c_int]),
     "ma_last_error": (C.c_char_p, []),

@@ -187,16 +187,8 @@ def muon_workspace_update(groups: Sequence[MuonGroup], hp: MuonHParams, workspac
     return flat.view(g.rows, ld.value)[:, : g.cols]
 
 
-def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] = None) -> None:
-    """One AdamW step. Each segment: param, grad, exp_avg, exp_avg_sq (fp32
-    tensors, contiguous), lr, beta1, beta2, eps, weight_decay, step (1-based).
-    With ``workgroups``, the same update by that many persistent workgroups
-    with a small register footprint (``ma_adamw_step_background``), for
-    running beside the Newton-Schulz GEMMs on another stream."""
-    if not segments:
-        return
+def _adamw_c(segments: Sequence[dict]):
     arr = (L.AdamWSegmentC * len(segments))()
-    dev = segments[0]["param"].device
     for i, s in enumerate(segments):
         p, g, m, v = s["param"], s["grad"], s["exp_avg"], s["exp_avg_sq"]
         for t in (p, g, m, v):
@@ -207,6 +199,19 @@ def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] 
                                  grad_dtype=_dt(g), lr=s["lr"], beta1=s.get("beta1", 0.9),
                                  beta2=s.get("beta2", 0.95), eps=s.get("eps", 1e-8),
                                  weight_decay=s.get("weight_decay", 0.0), step=int(s["step"]))
+    return arr
+
+
+def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] = None) -> None:
+    """One AdamW step. Each segment: param, grad, exp_avg, exp_avg_sq (fp32
+    tensors, contiguous), lr, beta1, beta2, eps, weight_decay, step (1-based).
+    With ``workgroups``, the same update by that many persistent workgroups
+    with a small register footprint (``ma_adamw_step_background``), for
+    running beside the Newton-Schulz GEMMs on another stream."""
+    if not segments:
+        return
+    arr = _adamw_c(segments)
+    dev = segments[0]["param"].device
     if workgroups is None:
         L.check(L.lib().ma_adamw_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
     else:
@@ -223,28 +228,34 @@ def optimizer_step(groups: Sequence[MuonGroup], hp: MuonHParams, adamw_segments:
     """One MuonAdamW step: ``muon_step`` over ``groups`` and ``adamw_step``
     over ``adamw_segments`` (disjoint buffers), both ordered after the work
     already on the current stream, with everything done once the current
-    stream reaches the end of the call. With ``overlap``, AdamW runs on a
-    second stream (default priority) by ``background_workgroups`` lean
-    workgroups while the Muon step runs on the current one, so that the
-    HBM-bound update shares the GPU with the MFMA-bound iteration; the
-    results are identical either way. Capturable in a HIP graph. Returns the
-    Muon workspace."""
-    if not adamw_segments:
-        return muon_step(groups, hp, workspace=workspace)
-    dev = adamw_segments[0]["param"].device
+    stream reaches the end of the call. With ``overlap`` (``ma_muon_adamw_step``),
+    AdamW runs on a second stream (default priority) by
+    ``background_workgroups`` lean workgroups beside the Muon step's
+    Newton-Schulz products, so that the HBM-bound update shares the GPU with
+    the MFMA-bound iteration; the results are identical either way.
+    Capturable in a HIP graph. Returns the Muon workspace."""
+    if not adamw_segments or not groups:
+        ws = muon_step(groups, hp, workspace=workspace) if groups else workspace
+        adamw_step(adamw_segments)
+        return ws
     if not overlap:
         ws = muon_step(groups, hp, workspace=workspace)
         adamw_step(adamw_segments)
         return ws
-    cur = torch.cuda.current_stream(dev)
+    dev = groups[0].device
+    need = muon_workspace_size(groups, hp)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     side = _SIDE.get(dev)
     if side is None:
         side = _SIDE[dev] = torch.cuda.Stream(device=dev)
-    side.wait_stream(cur)
-    adamw_step(adamw_segments, stream=side, workgroups=background_workgroups)
-    ws = muon_step(groups, hp, workspace=workspace)
-    cur.wait_stream(side)
-    return ws
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    arr = _adamw_c(adamw_segments)
+    L.check(L.lib().ma_muon_adamw_step(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
+                                       workspace.numel(), arr, len(adamw_segments), int(background_workgroups),
+                                       C.c_void_p(_stream(dev)), C.c_void_p(side.cuda_stream)))
+    return workspace
 
 
 def lion_step(segments: Sequence[dict], stream=None) -> None:

@@ -7,6 +7,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -308,8 +310,10 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
 // Enqueue T quintic steps for every group of the plan; X[0]/X^T[0] hold X0.
 // scaled (optional): per group, whether X0 holds Y with X0 = s Y, s in the
 // group's row-factor slot of row 0 of each matrix (k_finalize mode 4).
+// before_axpy (optional): called once, before the first AXPY launch is enqueued.
 int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
-               hipStream_t s, const std::vector<char>* scaled = nullptr) {
+               hipStream_t s, const std::vector<char>* scaled = nullptr,
+               const std::function<int()>* before_axpy = nullptr) {
   if (T == 0 || plan.g.empty()) return MA_OK;
   // groups with the most work per tile first (they set the tail of a launch)
   std::vector<int> order;
@@ -322,6 +326,10 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
     const int cur = step & 1, nxt = cur ^ 1;
     const bool last = step == T - 1;
     for (int epi = EPI_GRAM; epi <= EPI_AXPY; ++epi) {
+      if (step == 0 && epi == EPI_AXPY && before_axpy) {
+        const int rc = (*before_axpy)();
+        if (rc) return rc;
+      }
       NsTile tile = ns_tile(dtype, epi != EPI_AXPY);
       const bool qt = epi == EPI_AXPY && ns_q_transposed(dtype);
       tile.qt = qt ? 1 : 0;
@@ -499,8 +507,17 @@ bool pre_rows_for(const GroupPlan& p, const ma_muon_hparams* hp) {
 }
 
 namespace {
+// fork (optional): called once, when the first AXPY is about to be enqueued
+// (or after the last launch when there is none).
 int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
-                   size_t workspace_bytes, float* stats, void* stream) {
+                   size_t workspace_bytes, float* stats, void* stream,
+                   const std::function<int()>* fork = nullptr) {
+  bool forked = false;
+  std::function<int()> fork_once = [&]() -> int {
+    if (forked || !fork) return MA_OK;
+    forked = true;
+    return (*fork)();
+  };
   Plan plan;
   int rc = build_plan(groups, n_groups, hp, plan, true);
   if (rc) return rc;
@@ -567,7 +584,7 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
     }
   }
   // 4. T quintic steps
-  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s, &scaled);
+  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s, &scaled, &fork_once);
   if (rc) return rc;
   // 5. (MuonEq POST) and the update (and the update norms)
   const int ub = hp->ns_steps & 1;
@@ -600,7 +617,7 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
     }
     mat0 += p.count;
   }
-  return MA_OK;
+  return fork_once();
 }
 }  // namespace
 
@@ -643,7 +660,7 @@ int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups, cons
 }
 
 namespace {
-int adamw_impl(const ma_adamw_segment* segs, int32_t n, int32_t lean_blocks, void* stream) {
+int adamw_validate(const ma_adamw_segment* segs, int32_t n) {
   if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
   std::vector<Range> rs;
   for (int i = 0; i < n; ++i) {
@@ -666,8 +683,12 @@ int adamw_impl(const ma_adamw_segment* segs, int32_t n, int32_t lean_blocks, voi
     rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, 2});
     rs.push_back({(uintptr_t)S.exp_avg_sq, (uintptr_t)S.exp_avg_sq + nb, 2});
   }
-  int rc = check_overlaps(rs);
-  if (rc) return rc;
+  return check_overlaps(rs);
+}
+
+// Launches for segments that adamw_validate accepted.
+int adamw_enqueue(const ma_adamw_segment* segs, int32_t n, int32_t lean_blocks, void* stream) {
+  int rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   AdamArgs A{};
   int64_t blocks = 0;
@@ -715,7 +736,59 @@ int adamw_impl(const ma_adamw_segment* segs, int32_t n, int32_t lean_blocks, voi
   }
   return flush();
 }
+
+int adamw_impl(const ma_adamw_segment* segs, int32_t n, int32_t lean_blocks, void* stream) {
+  const int rc = adamw_validate(segs, n);
+  return rc ? rc : adamw_enqueue(segs, n, lean_blocks, stream);
+}
+
+// Two events per device and host thread for the fork and join of
+// ma_muon_adamw_step (created once, never destroyed, so that a step being
+// captured into a graph never sees one destroyed).
+int fork_events(hipEvent_t& e_fork, hipEvent_t& e_join) {
+  thread_local std::map<int, std::pair<hipEvent_t, hipEvent_t>> ev;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  auto it = ev.find(dev);
+  if (it == ev.end()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if ((err = hipEventCreateWithFlags(&a, hipEventDisableTiming)) != hipSuccess) return hip_fail(err, "event");
+    if ((err = hipEventCreateWithFlags(&b, hipEventDisableTiming)) != hipSuccess) return hip_fail(err, "event");
+    it = ev.emplace(dev, std::make_pair(a, b)).first;
+  }
+  e_fork = it->second.first;
+  e_join = it->second.second;
+  return MA_OK;
+}
 }  // namespace
+
+int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                       void* workspace, size_t workspace_bytes, const ma_adamw_segment* segs, int32_t n_segs,
+                       int32_t workgroups, void* stream, void* side_stream) {
+  if (workgroups < 1) return fail(MA_ERR_INVALID_ARG, "workgroups must be >= 1");
+  if (side_stream == stream) return fail(MA_ERR_INVALID_ARG, "side_stream must differ from stream");
+  int rc = adamw_validate(segs, n_segs);
+  if (rc) return rc;
+  hipEvent_t e_fork = nullptr, e_join = nullptr;
+  if ((rc = fork_events(e_fork, e_join))) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream), side = reinterpret_cast<hipStream_t>(side_stream);
+  // AdamW joins once the Muon step's elementwise passes and first GRAM and
+  // POLY are done: it then runs beside the AXPY and later products
+  std::function<int()> fork = [&]() -> int {
+    hipError_t err;
+    if ((err = hipEventRecord(e_fork, s)) != hipSuccess) return hip_fail(err, "fork record");
+    if ((err = hipStreamWaitEvent(side, e_fork, 0)) != hipSuccess) return hip_fail(err, "fork wait");
+    const int r = adamw_enqueue(segs, n_segs, workgroups, side_stream);
+    if (r) return r;
+    if ((err = hipEventRecord(e_join, side)) != hipSuccess) return hip_fail(err, "join record");
+    return MA_OK;
+  };
+  rc = muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, nullptr, stream, &fork);
+  if (rc) return rc;
+  const hipError_t err = hipStreamWaitEvent(s, e_join, 0);
+  return err == hipSuccess ? MA_OK : hip_fail(err, "join wait");
+}
 
 int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
   return adamw_impl(segs, n, 0, stream);

@@ -232,6 +232,22 @@ int ma_adamw_step(const ma_adamw_segment* segments, int32_t n_segments, void* st
 int ma_adamw_step_background(const ma_adamw_segment* segments, int32_t n_segments, int32_t workgroups,
                              void* stream);
 
+/* One MuonAdamW step: ma_muon_step on `stream` and, on `side_stream`, the
+ * AdamW update of ma_adamw_step_background (`workgroups` workgroups), which
+ * starts once the Muon step's elementwise passes and first Gram and
+ * polynomial products are done ("Chapter 4: The MuonAdamW Optimizer",
+ * section "The Full Muon Step": the two optimizers update disjoint parameter
+ * sets) and runs beside its remaining products; `stream` waits for it before
+ * any later work. Results are those of ma_muon_step followed by
+ * ma_adamw_step. side_stream must differ from stream (both may be captured
+ * into one HIP graph: the fork and join are event records and waits on
+ * events the library creates once per device and host thread). Every
+ * argument is validated before the first launch; Muon and AdamW buffers must
+ * not overlap. */
+int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                       void* workspace, size_t workspace_bytes, const ma_adamw_segment* segments,
+                       int32_t n_segments, int32_t workgroups, void* stream, void* side_stream);
+
 /* One flat Lion buffer. param, grad, exp_avg (the momentum, Lion's only
  * state): DEVICE pointers to n elements each, fp32 (param_dtype and
  * grad_dtype must be MA_F32), 4-byte aligned. */

@@ -201,6 +201,26 @@ def test_adamw_background_validates_workgroups():
     assert L.lib().ma_adamw_step_background(None, 0, 256, None) == 0
 
 
+def test_muon_adamw_step_validates_before_launch():
+    g, k = group(rows=64, cols=128, count=2)
+    h, t = hp()
+    garr = (L.MuonGroupC * 1)(g)
+    seg = L.AdamWSegmentC(param=BASE * 2, grad=BASE * 2 + (1 << 24), exp_avg=BASE * 2 + (2 << 24),
+                          exp_avg_sq=BASE * 2 + (3 << 24), n=1000, param_dtype=0, grad_dtype=0, lr=1e-3,
+                          beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=1)
+    arr = (L.AdamWSegmentC * 1)(seg)
+    lib = L.lib()
+    ws, nb = C.c_void_p(BASE * 4), 1 << 40
+    s1, s2 = C.c_void_p(0x1000), C.c_void_p(0x2000)
+    assert lib.ma_muon_adamw_step(garr, 1, C.byref(h), ws, nb, arr, 1, 0, s1, s2) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_muon_adamw_step(garr, 1, C.byref(h), ws, nb, arr, 1, 256, s1, s1) == L.MA_ERR_INVALID_ARG
+    bad = L.AdamWSegmentC(param=BASE * 2, grad=BASE * 2, exp_avg=BASE * 2 + (2 << 24),   # grad aliases param
+                          exp_avg_sq=BASE * 2 + (3 << 24), n=1000, param_dtype=0, grad_dtype=0, lr=1e-3,
+                          beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=1)
+    assert lib.ma_muon_adamw_step(garr, 1, C.byref(h), ws, nb, (L.AdamWSegmentC * 1)(bad), 1, 256, s1,
+                                  s2) == L.MA_ERR_INVALID_ARG
+
+
 def test_adamw_zero_segments_is_noop():
     assert L.lib().ma_adamw_step(None, 0, None) == L.MA_OK
     arr = (L.AdamWSegmentC * 1)(seg(n=0, param=None, grad=None, exp_avg=None, exp_avg_sq=None))

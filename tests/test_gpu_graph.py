@@ -96,3 +96,25 @@ def test_graph_replays_match_eager_steps(overlap):
         a, b = _snapshot(em, ea), _snapshot(gm, ga)
         for i, (x, y) in enumerate(zip(a, b)):
             assert np.array_equal(x, y), f"replay {k}: tensor {i} differs from the eager step"
+
+
+def test_overlapped_step_matches_sequential_step():
+    """Eager: AdamW on a second stream beside the Muon step (ma_muon_adamw_step)
+    gives the bits of the Muon step followed by the AdamW step, over 3 steps."""
+    need_gpu()
+    import adamw_optimizer_step_amd as M
+    init_m, init_a = _state(5)
+    outs = []
+    for overlap in (False, True):
+        dm, da = _to_dev(init_m, init_a)
+        groups, hp, _ = _stepper(M, dm, da, None)
+        ws = torch.empty(max(1, M.muon_workspace_size(groups, hp)), dtype=torch.uint8, device=DEV)
+        _, _, step = _stepper(M, dm, da, ws, overlap=overlap)
+        for _k in range(3):
+            step()
+        torch.cuda.synchronize()
+        outs.append(_snapshot(dm, da))
+    say("overlapped vs sequential eager steps")
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
