@@ -311,6 +311,10 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
 // scaled (optional): per group, whether X0 holds Y with X0 = s Y, s in the
 // group's row-factor slot of row 0 of each matrix (k_finalize mode 4).
 // before_axpy (optional): called once, before the first AXPY launch is enqueued.
+#ifndef MA_FORK_AT
+#define MA_FORK_AT 2
+#endif
+constexpr int kForkAt = MA_FORK_AT;   // 3 * step + product (GRAM 0, POLY 1, AXPY 2)
 int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
                hipStream_t s, const std::vector<char>* scaled = nullptr,
                const std::function<int()>* before_axpy = nullptr) {
@@ -326,7 +330,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
     const int cur = step & 1, nxt = cur ^ 1;
     const bool last = step == T - 1;
     for (int epi = EPI_GRAM; epi <= EPI_AXPY; ++epi) {
-      if (step == 0 && epi == EPI_AXPY && before_axpy) {
+      if (step * 3 + epi == kForkAt && before_axpy) {
         const int rc = (*before_axpy)();
         if (rc) return rc;
       }
