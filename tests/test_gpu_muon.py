@@ -212,7 +212,8 @@ def test_ragged_groups(eq, cautious, wd, dts):
 
 
 @pytest.mark.parametrize("steps", [0, 5])
-@pytest.mark.parametrize("dts", [("f32", "f32", "f32"), ("bf16", "bf16", "bf16"), ("bf16", "bf16", "f32")])
+@pytest.mark.parametrize("dts", [("f32", "f32", "f32"), ("bf16", "bf16", "bf16"), ("bf16", "bf16", "f32"),
+                                 ("bf16", "f32", "f32")])
 def test_row_norms_of_long_rows(steps, dts):
     """MuonEq row factors for rows of one to seventeen 512-column chunks:
     1024 columns (two chunks, four rows read together), 1536 (three of a
@@ -238,6 +239,10 @@ def test_row_norms_of_long_rows(steps, dts):
              coeffs=KJ)
     say("long rows", steps, dts)
     dev, mgs, ws = _run_step(groups_np, hp, dts)
+    if prec == "bf16" and steps > 0:
+        # the 1024- and 1536-column groups take the one-pass form, the rest two passes
+        import adamw_optimizer_step_amd as M
+        assert [M.muon_row_pass(mgs, hp, i) for i in range(len(mgs))] == [True, True, False, False, False]
     _check_step(groups_np, dev, mgs, ws, hp, dts)
 
 
