@@ -979,6 +979,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_pe
 ns_gemm_dma(const NsArgs args) {
   using namespace dma;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES];
+  // issue priority over waves of other kernels sharing the CU (the AdamW
+  // update that may run beside the iteration on another stream, at priority 0)
+  __builtin_amdgcn_s_setprio(1);
   const int x = (int)(blockIdx.x & 7);
   const int P = (int)(gridDim.x >> 3);
   TileJob J;
