@@ -13,12 +13,12 @@ Sources, in the order the step runs:
 3. Frobenius normalisation ``X0 = M / (||M||_F + 1e-7)``: "Chapter 4", section
    "Polar Express: Newton-Schulz Orthogonalization"; "3.9 Optimizers", section
    "Muon: Orthogonalizing the Update".
-4. Orientation: a matrix with more rows than columns is iterated transposed,
-   so that ``X X^T`` is the smaller Gram matrix (same two sections).
-5. ``T`` quintic steps ``A = X X^T; B = b A + c A A; X = a X + B X`` with a
-   per-step coefficient triple (same two sections; Polar Express uses a
-   different triple at each step, per the nanochat discussion).
-6. Cautious decoupled weight decay and the update ``W - lr_eff*wd*mask*W -
+4. ``T`` quintic steps, each the odd polynomial ``a X + b (X X^T) X + c (X
+   X^T)^2 X`` with a per-step coefficient triple (same two sections; Polar
+   Express uses a different triple at each step, per the nanochat
+   discussion), evaluated through the smaller Gram matrix: ``X X^T`` when
+   the matrix has no more rows than columns, ``X^T X`` otherwise.
+5. Cautious decoupled weight decay and the update ``W - lr_eff*wd*mask*W -
    lr_eff*U`` with ``mask = (U * W >= 0)`` and ``lr_eff = lr *
    sqrt(max(1, rows/cols))``: nanochat discussion (mask and multiplier);
    "Chapter 4", section "The Full Muon Step" (decay uses the weight before
@@ -29,10 +29,11 @@ Precision modes of the Newton-Schulz part (``precision``):
 * ``"f64"``: no rounding anywhere -- the reference for fp32-mode parity;
 * ``"f32"``: X0 and every product in binary32 (numpy sgemm);
 * ``"bf16"``: the rounding points of the bf16 GPU path. X0 is rounded to
-  bf16; ``A = X X^T`` is formed exactly (float64 sums of exact products of
-  bf16 values, standing in for an fp32 accumulator) and rounded to bf16;
-  ``B = b*A + c*(A A)`` likewise from the rounded A; ``X' = a*X + B X``
-  likewise from the rounded B and X.
+  bf16; the Gram matrix ``A`` (``X X^T``, or ``X^T X`` for a tall matrix) is
+  formed exactly (float64 sums of exact products of bf16 values, standing in
+  for an fp32 accumulator) and rounded to bf16; ``B = b*A + c*(A A)`` likewise
+  from the rounded A, rounded once; ``X' = a*X + B X`` (tall: ``a*X + X B``)
+  likewise from the rounded B and X, rounded once.
 
 The elementwise parts (momentum, decay, update) are binary32 with one rounding
 per operation and no fused multiply-add; they are the bit-exact contract.
@@ -148,32 +149,33 @@ def _round(x, precision):
 def newton_schulz(x0, coeffs, precision: str = "f64", ns_steps=None):
     """Quintic Newton-Schulz / Polar Express iteration on ``x0`` (param layout).
 
-    Transposes first when ``x0`` has more rows than columns and transposes the
-    result back, so the output has ``x0``'s shape. ``x0`` is rounded to the
-    working precision first (bf16 mode: to bf16).
+    One step replaces X by the odd matrix polynomial
+    ``p(X) = a X + b (X X^T) X + c (X X^T)^2 X``: with ``X = U diag(s) V^T`` it
+    maps each singular value s to ``a s + b s^3 + c s^5`` and keeps U and V
+    ("Muon vs AdamW, Lion and Sophia: a fair race", section "Muon"; "3.9
+    Optimizers ...", section "Muon: Orthogonalizing the Update"). Because
+    ``(X X^T) X = X (X^T X)``, the polynomial is evaluated through the smaller
+    Gram matrix, as both pages prescribe for the cost ("Chapter 4", section
+    "Polar Express: Newton-Schulz Orthogonalization"):
+
+    * rows <= cols: ``G = X X^T``, ``B = b G + c G G``, ``p(X) = a X + B X``;
+    * rows >  cols: ``G = X^T X``, ``B = b G + c G G``, ``p(X) = a X + X B``.
+
+    Rounding (``precision``): "f64" rounds nowhere; "f32" keeps every array and
+    coefficient in binary32 (numpy sgemm); "bf16" rounds ``x0`` to bf16 and
+    then, at each step, G, B and the new X once each (exact float64 products of
+    bf16 values stand in for the fp32 accumulator; one rounding to binary32,
+    then to bf16). The result has ``x0``'s shape.
     """
     steps = coefficient_schedule(coeffs, ns_steps)
     X = _round(x0, precision)
-    transposed = X.shape[0] > X.shape[1]
-    if transposed:
-        X = X.T
-    if precision == "f32":
-        for a, b, c in steps:
-            A = X @ X.T
-            B = f32(b) * A + f32(c) * (A @ A)
-            X = f32(a) * X + B @ X
-    elif precision == "f64":
-        for a, b, c in steps:
-            A = X @ X.T
-            B = b * A + c * (A @ A)
-            X = a * X + B @ X
-    else:  # bf16 rounding points, exact accumulation
-        for a, b, c in steps:
-            A = _round(X @ X.T, "bf16")
-            B = _round(b * A + c * (A @ A), "bf16")
-            X = _round(a * X + B @ X, "bf16")
-    if transposed:
-        X = X.T
+    wide = X.shape[0] <= X.shape[1]
+    rnd = (lambda Y: _round(Y, "bf16")) if precision == "bf16" else (lambda Y: Y)
+    k = f32 if precision == "f32" else float
+    for a, b, c in steps:
+        G = rnd(X @ X.T if wide else X.T @ X)
+        B = rnd(k(b) * G + k(c) * (G @ G))
+        X = rnd(k(a) * X + (B @ X if wide else X @ B))
     return np.ascontiguousarray(X)
 
 
