@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3_12L_d1024")
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--adamw-workgroups", type=int, default=256,
                     help="workgroups of the AdamW update when it runs beside the Muon step")
     ap.add_argument("--no-practical", action="store_true", help="skip the practical-peak calibration kernels")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip the latency lines of the single 256x1024 matrix and the 4-layer d=256 set")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed steps, run 3 plain device copies of MIB MiB (read MIB, write MIB) "
                          "as the known-size reference that scales HBM byte counters")
@@ -166,37 +168,19 @@ def main():
     torch.cuda.synchronize()
     if profile:
         L.check(lib.ma_profile_end())
-    ms = marks[0].elapsed_time(marks[-1]) / args.steps
-    ms_eager = ms
-    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    ms_eager = marks[0].elapsed_time(marks[-1]) / args.steps
+    eager_q = quantiles([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    print(f"[bench] timed {args.steps} steps: {ms_eager:.3f} ms/step", file=sys.stderr, flush=True)
 
     # The same step captured once in a HIP graph and replayed: the kernels
     # and their arguments are those of one eager step (the AdamW step count,
     # a host scalar, stays at its captured value), with the launch gaps gone.
     ms_graph = None
+    graph_q = None
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(dev)
-        cap.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(cap):
-            step(args.warmup + args.steps)          # warm the capture stream
-        torch.cuda.current_stream(dev).wait_stream(cap)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            step(args.warmup + args.steps)
-        g.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        ms_graph = g0.elapsed_time(g1) / args.steps
-        print(f"[bench] graph replay: {ms_graph:.3f} ms/step", file=sys.stderr, flush=True)
-        ms = min(ms, ms_graph)
+        ms_graph, per_replay = graph_timing(torch, dev, lambda: step(args.warmup + args.steps), args.steps)
+        graph_q = quantiles(per_replay)
+        print(f"[bench] graph replay: {ms_graph:.3f} ms/step (median {graph_q[1]:.3f})", file=sys.stderr, flush=True)
 
     # per-kernel durations from the events recorded around each launch
     import ctypes as C
@@ -257,6 +241,11 @@ def main():
         key = "mfma_bf16" if roofline["bound"] == "mfma" else "copy"
         if roofline["unit"] == practical[key]["unit"] and roofline.get("achieved"):
             roofline["frac_of_practical_peak"] = round(roofline["achieved"] / practical[key]["achieved"], 4)
+    # the reported step time: the median step of the faster timing mode
+    use_graph = graph_q is not None and graph_q[1] < eager_q[1]
+    q = graph_q if use_graph else eager_q
+    ms = q[1]
+    latency = None if args.no_latency else latency_lines(M, torch, dev, args.steps)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, T, args.cpu_budget_s)
     out = {
         "metric": "Muon+AdamW full steps/sec at 12L d=1024; NS-GEMM MFMA util %; HBM GB/s",
@@ -278,11 +267,13 @@ def main():
                    "parallelism": "single GPU",
                    "streams": ("AdamW on a second stream beside the Muon step" if (data["adamw"] and not args.no_overlap)
                                else "one stream"),
-                   "timing": ("HIP-graph replay of one captured step" if ms_graph is not None and ms == ms_graph
-                              else "eager launches"),
-                   "ms_per_step_eager": round(ms_eager, 4),
-                   "eager_step_ms_p10_median_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
-                   "ms_per_step_graph": round(ms_graph, 4) if ms_graph is not None else None,
+                   "timing": ("median of HIP-graph replays of one captured step" if use_graph
+                              else "median of eager steps"),
+                   "step_ms_p10_median_p90": [round(v, 4) for v in q],
+                   "ms_per_step_eager_mean": round(ms_eager, 4),
+                   "eager_step_ms_p10_median_p90": [round(v, 4) for v in eager_q],
+                   "ms_per_step_graph_mean": round(ms_graph, 4) if ms_graph is not None else None,
+                   "graph_step_ms_p10_median_p90": [round(v, 4) for v in graph_q] if graph_q else None,
                    "kernel_timing": "per-kernel HIP events inside the eager timed steps" if profile
                    else "no per-kernel events"},
         "roofline": roofline,
@@ -292,10 +283,92 @@ def main():
                     "mfma_util": round(model["ns_total_flops_per_step"] / (ns_ms * 1e-3) / 1e12 / peak_f, 4) if ns_ms else None},
         "kernels": kernels,
         "lion": lion,
+        "latency": latency,
         "practical_peaks": practical,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def quantiles(xs):
+    """(p10, median, p90) of a list of step times."""
+    v = sorted(xs)
+    at = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return at(0.1), at(0.5), at(0.9)
+
+
+def graph_timing(torch, dev, step, n):
+    """One call of ``step`` captured in a HIP graph (after a warm-up call on the
+    capture stream), replayed ``n`` times with an event pair around each replay.
+    Returns (whole-run mean ms, per-replay ms)."""
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    mean = ev[0].elapsed_time(ev[-1]) / n
+    del g
+    return mean, per
+
+
+def latency_lines(M, torch, dev, n):
+    """Latency of one whole optimizer step on the two small configurations,
+    which launch and latency bound (they cannot fill 256 CUs): the single fp32
+    256 x 1024 matrix (5 steps of the fp32 iteration) and the 4-layer d=256 set
+    (bf16 Muon with AdamW beside it). Median and p10/p90 over ``n`` steps, eager
+    and as graph replays, in microseconds."""
+    from workloads import materialize, workload
+    out = {}
+    for name in ("c1_256x1024_f32", "c2_4L_d256"):
+        wl = workload(name)
+        data = materialize(wl, device=dev, seed=0)
+        groups = [M.MuonGroup(d["W"], d["G"], d["M"]) for d in data["muon"]]
+        hp = M.MuonHParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
+                           ns_steps=wl.ns_steps, coeffs=M.KELLER_JORDAN, cautious=wl.cautious,
+                           equilibrate=wl.equilibrate, ns_precision=wl.ns_precision, lr_scale=wl.lr_scale)
+        ws = torch.empty(max(1, M.muon_workspace_size(groups, hp)), dtype=torch.uint8, device=dev)
+        segs = [dict(param=a["p"], grad=a["g"], exp_avg=a["m"], exp_avg_sq=a["v"], step=a["step"], lr=a["spec"].lr,
+                     beta1=a["spec"].beta1, beta2=a["spec"].beta2, eps=a["spec"].eps,
+                     weight_decay=a["spec"].weight_decay) for a in data["adamw"]]
+        step = lambda: M.optimizer_step(groups, hp, segs, workspace=ws, overlap=bool(segs))
+        for _ in range(10):
+            step()
+        stream = torch.cuda.current_stream(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        eager = quantiles([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+        _, per = graph_timing(torch, dev, step, n)
+        graph = quantiles(per)
+        out[name] = {"description": wl.description, "unit": "us",
+                     "eager_p10_median_p90": [round(1e3 * v, 1) for v in eager],
+                     "graph_p10_median_p90": [round(1e3 * v, 1) for v in graph],
+                     "ns_gflop": round(wl.ns_steps * sum(g.count * (3 * min(g.rows, g.cols) ** 2 * max(g.rows, g.cols)
+                                                                   + min(g.rows, g.cols) ** 3)
+                                                          for g in wl.muon_groups) / 1e9, 3)}
+        del data, groups, ws, segs
+        torch.cuda.empty_cache()
+        print(f"[bench] latency {name}: eager {out[name]['eager_p10_median_p90'][1]} us, "
+              f"graph {out[name]['graph_p10_median_p90'][1]} us", file=sys.stderr, flush=True)
+    return out
 
 
 def practical_peaks(L, lib, dev):
