@@ -3,7 +3,9 @@ from the exact result U phi(s/||s||) V^T on the largest single-GPU share
 (32 layers of d=4096: groups of 4096^2, 16384x4096 and 4096x16384 matrices
 with power-law spectrum s_i ~ 1/i), for the matrices the full-size GPU test
 checks (first and last of every group, input seed 0, zero momentum, no row
-equilibration, five steps of the (3.4445, -4.7750, 2.0315) quintic).
+equilibration, 1, 3 and 5 steps of the (3.4445, -4.7750, 2.0315) quintic:
+the ns_steps sweep of the nanochat discussion "Stuck at the optimizer after
+figuring out backward()", reply by mira687).
 
 The exact result follows from the scalar form of the iteration: every step
 maps each singular value through the same odd quintic and leaves the
@@ -12,7 +14,7 @@ section "Muon"). The distance is the relative Frobenius norm of
 U^T Y V - diag(phi), computed with the Kronecker factors.
 
 Run from the repository root: python tests/golden/make_closed_form_bf16_error.py
-(about ten minutes on eight host cores). Calls only the oracle and the
+(about twenty minutes on eight host cores). Calls only the oracle and the
 seeded input generators.
 """
 import json
@@ -53,27 +55,29 @@ def main():
     cases = []
     for gi, spec in enumerate(wl.muon_groups):
         for k in sorted({0, spec.count - 1}):
-            t0 = time.time()
             f = grad_factors(wl, gi, k, seed=0)
             g = O.round_to_bf16(kron_spectrum_matrix(f, "cpu", torch.float64).numpy().astype(np.float32))
             _, mt = O.momentum_stage(g, np.zeros_like(g), wl.momentum, wl.nesterov)
             x0 = O.normalize(mt, "off", 1e-7)
-            Y = O.newton_schulz(x0, KJ, "bf16", wl.ns_steps).astype(np.float64)
-            D = rotate(Y, f)
             s = f[4].numpy()
-            phi = O.scalar_polynomial(s / np.linalg.norm(s), KJ, wl.ns_steps)
-            err = float(np.linalg.norm(D - np.diag(phi)) / np.linalg.norm(phi))
-            top = float(np.max(np.abs(np.diag(D)[:64] - phi[:64]) / phi[:64]))
-            cases.append({"group": gi, "rows": spec.rows, "cols": spec.cols, "matrix": k,
-                          "rel_fro": round(err, 6), "top64_rel": round(top, 6)})
-            print(cases[-1], f"{time.time() - t0:.0f}s", flush=True)
+            for T in (1, 3, 5):
+                t0 = time.time()
+                Y = O.newton_schulz(x0, KJ, "bf16", T).astype(np.float64)
+                D = rotate(Y, f)
+                phi = O.scalar_polynomial(s / np.linalg.norm(s), KJ, T)
+                err = float(np.linalg.norm(D - np.diag(phi)) / np.linalg.norm(phi))
+                top = float(np.max(np.abs(np.diag(D)[:64] - phi[:64]) / phi[:64]))
+                cases.append({"ns_steps": T, "group": gi, "rows": spec.rows, "cols": spec.cols, "matrix": k,
+                              "rel_fro": round(err, 6), "top64_rel": round(top, 6)})
+                print(cases[-1], f"{time.time() - t0:.0f}s", flush=True)
     doc = {
         "source": "scalar form of the quintic iteration: singular values pass through the composed "
                   "polynomial, singular vectors are kept -- Muon vs AdamW, Lion and Sophia: a fair race, "
                   "section 'Muon'",
         "what": "relative Frobenius distance of the bf16-emulating oracle's Newton-Schulz output from "
                 "U phi(s/||s||) V^T, and the largest relative error among the 64 largest singular values",
-        "workload": "32 layers d=4096, input seed 0, zero momentum, equilibration off, 5 steps of (3.4445, -4.7750, 2.0315)",
+        "workload": "32 layers d=4096, input seed 0, zero momentum, equilibration off, 1, 3 and 5 steps of "
+                    "(3.4445, -4.7750, 2.0315)",
         "command": "python tests/golden/make_closed_form_bf16_error.py",
         "cases": cases,
     }

@@ -43,13 +43,15 @@ DEV = torch.device("cuda:0")
 KJ = (3.4445, -4.7750, 2.0315)
 
 
+# the GPU's distance to the closed form may exceed the bf16 oracle's own by this factor
+RATIO = 1.25
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_form_bf16_error.json")
 
 
 def _oracle_distance():
-    """(group, matrix) -> the oracle's relative distance to the closed form."""
+    """(ns_steps, group, matrix) -> the oracle's relative distance to the closed form."""
     with open(GOLDEN) as fh:
-        return {(c["group"], c["matrix"]): c["rel_fro"] for c in json.load(fh)["cases"]}
+        return {(c.get("ns_steps", 5), c["group"], c["matrix"]): c["rel_fro"] for c in json.load(fh)["cases"]}
 
 
 def _hp(M, wl, **kw):
@@ -74,16 +76,20 @@ def _rotate(Y, factors):
     return T.reshape(m1 * m2, m1 * m2)
 
 
-def test_largest_share_closed_form():
+@pytest.mark.parametrize("ns_steps", [1, 3, 5])
+def test_largest_share_closed_form(ns_steps):
+    """The ns_steps sweep {1, 3, 5} of the nanochat discussion ("Stuck at the
+    optimizer after figuring out backward()", reply by mira687) at the
+    largest single-GPU share."""
     need_gpu()
     import adamw_optimizer_step_amd as M
-    wl = workload("c5_32L_d4096").scaled(mom_init="zero", equilibrate="off")
-    say("largest share: inputs")
+    wl = workload("c5_32L_d4096").scaled(mom_init="zero", equilibrate="off", ns_steps=ns_steps)
+    say("largest share: inputs", ns_steps)
     data = materialize(wl, device=DEV, seed=0)
     mgs = [M.MuonGroup(d["W"], d["G"], d["M"]) for d in data["muon"]]
     hp = _hp(M, wl)
     ref = _oracle_distance()
-    say("largest share: step", [m.count for m in mgs])
+    say("largest share: step", ns_steps, [m.count for m in mgs])
     ws = M.muon_step(mgs, hp)
     torch.cuda.synchronize()
     for gi, d in enumerate(data["muon"]):
@@ -96,7 +102,8 @@ def test_largest_share_closed_form():
             say("largest share: closed form", gi, k, tuple(Y.shape))
             D = _rotate(Y, f)
             err = float(torch.linalg.matrix_norm(D - torch.diag(phi)) / torch.linalg.vector_norm(phi))
-            bound = 1.25 * ref[(gi, k)]
+            bound = RATIO * ref[(ns_steps, gi, k)]
+            say("largest share: closed form", ns_steps, gi, k, f"gpu {err:.5f}", f"oracle {ref[(ns_steps, gi, k)]:.5f}")
             assert err <= bound, f"group {gi} matrix {k}: relative distance to U phi V^T {err:.4f} > {bound:.4f}"
             top = float((torch.diagonal(D)[:64] - phi[:64]).abs().div(phi[:64]).max())
             assert top <= 2e-2, f"group {gi} matrix {k}: top-64 singular values off by {top:.4f}"
