@@ -42,6 +42,52 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Host-side sanitizers for the planner and argument validation (api.hip, the
+# host code of the C ABI): each flag applies to the host compilation only, so
+# the device code is the same as in the product library. The result is a
+# separate library for CPU-only tests, loaded with the ASan runtime preloaded.
+HOST_SANITIZE = ["-Xarch_host -fsanitize=address", "-Xarch_host -fsanitize=undefined",
+                 "-Xarch_host -fno-sanitize-recover=undefined", "-Xarch_host -fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "host_sanitized", "libmuon_adamw_hostsan.so")
+
+
+def build_host_sanitized(verbose: bool = True) -> str:
+    """``libmuon_adamw_hostsan.so``: the library with api.hip's host code built
+    under AddressSanitizer and UndefinedBehaviorSanitizer (for CPU tests of the
+    ABI; run it with the ASan runtime preloaded, see ``asan_runtime``)."""
+    out = os.path.dirname(SAN_LIB)
+    os.makedirs(out, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = []
+    for src in sources:
+        if os.path.basename(src) == "api.hip":
+            obj = os.path.join(out, "api.hip.o")
+            flags = FLAGS + [f for pair in HOST_SANITIZE for f in pair.split()]
+            r = subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+            objs.append(obj)
+        else:
+            # the other sources' objects of the product build, when current
+            obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+            fresh = os.path.exists(obj) and os.path.getmtime(obj) >= max(
+                os.path.getmtime(f) for f in glob.glob(os.path.join(CSRC, "*")))
+            objs.append(obj if fresh else _compile(src))
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", SAN_LIB],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to LD_PRELOAD)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -60,4 +106,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build_host_sanitized() if "--host-sanitized" in sys.argv else build()
