@@ -16,6 +16,7 @@ MA_ERR_INVALID_ARG = -1
 MA_ERR_UNSUPPORTED = -2
 MA_ERR_WORKSPACE = -3
 MA_ERR_HIP = -4
+MA_ERR_NONFINITE = -5
 
 MA_F32 = 0
 MA_BF16 = 1
@@ -41,6 +42,7 @@ class MuonHParamsC(C.Structure):
         ("nesterov", C.c_int32), ("ns_steps", C.c_int32), ("abc", C.POINTER(C.c_float)),
         ("cautious", C.c_int32), ("equilibrate", C.c_int32), ("ns_precision", C.c_int32),
         ("lr_scale", C.c_int32), ("norm_eps", C.c_float), ("eq_eps", C.c_float),
+        ("check_finite", C.c_int32),
     ]
 
 
@@ -67,6 +69,8 @@ EXPORTS = {
                                C.c_size_t, C.c_void_p]),
     "ma_muon_step_stats": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
                                      C.c_size_t, C.c_void_p, C.c_void_p]),
+    "ma_muon_nonfinite": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
+                                    C.c_void_p]),
     "ma_muon_row_pass": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_int32]),
     "ma_muon_workspace_update": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC),
                                            C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_void_p),
@@ -90,6 +94,7 @@ EXPORTS = {
                                         C.c_void_p]),
     "ma_test_muon_update": (C.c_int, [C.POINTER(MuonGroupC), C.c_void_p, C.c_int32, C.c_float,
                                       C.c_float, C.c_int32, C.c_int32, C.c_void_p]),
+    "ma_test_fail_after_fork": (C.c_int, []),
     "ma_test_ns_workspace_size": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int32, C.c_int32]),
     "ma_test_ns": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                              C.POINTER(C.c_float), C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),

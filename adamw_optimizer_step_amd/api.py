@@ -52,6 +52,7 @@ class MuonHParams:
     lr_scale: str = "sqrt_max1_r_over_c"
     norm_eps: float = 1e-7
     eq_eps: float = 1e-7
+    check_finite: bool = False         # flag matrices with non-finite norms (see muon_nonfinite)
 
     def table(self) -> List[float]:
         c = list(self.coeffs)
@@ -69,7 +70,8 @@ class MuonHParams:
             nesterov=int(bool(self.nesterov)), ns_steps=int(self.ns_steps),
             abc=C.cast(arr, C.POINTER(C.c_float)), cautious=int(bool(self.cautious)),
             equilibrate=_EQ[self.equilibrate], ns_precision=_PREC[self.ns_precision],
-            lr_scale=_SCALE[self.lr_scale], norm_eps=self.norm_eps, eq_eps=self.eq_eps)
+            lr_scale=_SCALE[self.lr_scale], norm_eps=self.norm_eps, eq_eps=self.eq_eps,
+            check_finite=int(bool(self.check_finite)))
         return hp, arr
 
 
@@ -89,14 +91,53 @@ def _matrix_ptrs(x: Union[torch.Tensor, Sequence[torch.Tensor]], rows: int, cols
     return out
 
 
+def _check_dense(g):
+    if g.layout != torch.strided:
+        # as an optimizer's step() does for sparse gradients ("3.9 Optimizers",
+        # section "Implementing AdamW from scratch")
+        raise TypeError("sparse gradients are not supported")
+
+
+def _as_list(x):
+    if isinstance(x, torch.Tensor):
+        return [x] if x.dim() == 2 else [x[i] for i in range(x.shape[0])]
+    return list(x)
+
+
+def _drop_missing(params, grads, momentum):
+    """Matrices whose gradient is None are left out of the step (as an
+    optimizer's step() skips parameters without a gradient, "3.9 Optimizers",
+    section "Implementing AdamW from scratch"). Returns the kept params,
+    grads and momentum and their indices."""
+    if isinstance(grads, torch.Tensor):
+        _check_dense(grads)
+        return params, grads, momentum, list(range(1 if grads.dim() == 2 else grads.shape[0]))
+    P, Mo = _as_list(params), _as_list(momentum)
+    G = [None] * len(P) if grads is None else list(grads)
+    if not (len(P) == len(G) == len(Mo)):
+        raise ValueError("params, grads and momentum differ in count")
+    keep = [i for i, g in enumerate(G) if g is not None]
+    for i in keep:
+        _check_dense(G[i])
+    return [P[i] for i in keep], [G[i] for i in keep], [Mo[i] for i in keep], keep
+
+
 class MuonGroup:
-    """``count`` same-shape matrices: stacked ``[count, R, C]`` tensors or lists."""
+    """``count`` same-shape matrices: stacked ``[count, R, C]`` tensors or lists.
+
+    A gradient of ``None`` (a list entry, or ``grads=None`` for the whole
+    group) leaves that matrix out of the step: its weight and momentum are not
+    touched. ``kept`` lists the indices that take part. Sparse gradients are
+    rejected."""
 
     def __init__(self, params, grads, momentum):
         first = params if isinstance(params, torch.Tensor) else params[0]
         self.rows, self.cols = int(first.shape[-2]), int(first.shape[-1])
         self.device = first.device
-        self.dtypes = tuple(_dt(t if isinstance(t, torch.Tensor) else t[0]) for t in (params, grads, momentum))
+        self.dtypes = tuple(_dt(t if isinstance(t, torch.Tensor) else t[0]) for t in (params, momentum))
+        params, grads, momentum, self.kept = _drop_missing(params, grads, momentum)
+        gd = grads if isinstance(grads, torch.Tensor) else (grads[0] if grads else None)
+        self.dtypes = (self.dtypes[0], _dt(gd) if gd is not None else self.dtypes[0], self.dtypes[1])
         self.p = _matrix_ptrs(params, self.rows, self.cols)
         self.g = _matrix_ptrs(grads, self.rows, self.cols)
         self.m = _matrix_ptrs(momentum, self.rows, self.cols)
@@ -160,6 +201,21 @@ def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[
     return workspace
 
 
+def muon_nonfinite(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: torch.Tensor) -> List[bool]:
+    """After a step with ``hp.check_finite`` (waits for the device): per matrix
+    of ``groups`` (in order), whether its look-ahead momentum had non-finite
+    norms, so that its weight was left unchanged (``ma_muon_nonfinite``)."""
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    total = sum(g.count for g in groups)
+    flags = (C.c_int32 * max(1, total))()
+    torch.cuda.synchronize(groups[0].device) if groups else None
+    rc = L.lib().ma_muon_nonfinite(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()), flags)
+    if rc not in (L.MA_OK, L.MA_ERR_NONFINITE):
+        L.check(rc)
+    return [bool(flags[i]) for i in range(total)]
+
+
 def muon_row_pass(groups: Sequence[MuonGroup], hp: MuonHParams, group: int) -> bool:
     """Whether ``muon_step`` reads group ``group``'s G and M once (momentum,
     MuonEq row sums and X0 in one pass, the Frobenius factor applied by the
@@ -188,7 +244,11 @@ def muon_workspace_update(groups: Sequence[MuonGroup], hp: MuonHParams, workspac
 
 
 def _adamw_c(segments: Sequence[dict]):
-    arr = (L.AdamWSegmentC * len(segments))()
+    # a segment whose gradient is None takes no step; sparse gradients are rejected
+    segments = [s for s in segments if s["grad"] is not None]
+    for s in segments:
+        _check_dense(s["grad"])
+    arr = (L.AdamWSegmentC * max(1, len(segments)))()
     for i, s in enumerate(segments):
         p, g, m, v = s["param"], s["grad"], s["exp_avg"], s["exp_avg_sq"]
         for t in (p, g, m, v):
@@ -199,7 +259,7 @@ def _adamw_c(segments: Sequence[dict]):
                                  grad_dtype=_dt(g), lr=s["lr"], beta1=s.get("beta1", 0.9),
                                  beta2=s.get("beta2", 0.95), eps=s.get("eps", 1e-8),
                                  weight_decay=s.get("weight_decay", 0.0), step=int(s["step"]))
-    return arr
+    return arr, len(segments)
 
 
 def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] = None) -> None:
@@ -210,13 +270,12 @@ def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] 
     running beside the Newton-Schulz GEMMs on another stream."""
     if not segments:
         return
-    arr = _adamw_c(segments)
+    arr, n = _adamw_c(segments)
     dev = segments[0]["param"].device
     if workgroups is None:
-        L.check(L.lib().ma_adamw_step(arr, len(segments), C.c_void_p(_stream(dev, stream))))
+        L.check(L.lib().ma_adamw_step(arr, n, C.c_void_p(_stream(dev, stream))))
     else:
-        L.check(L.lib().ma_adamw_step_background(arr, len(segments), int(workgroups),
-                                                 C.c_void_p(_stream(dev, stream))))
+        L.check(L.lib().ma_adamw_step_background(arr, n, int(workgroups), C.c_void_p(_stream(dev, stream))))
 
 
 _SIDE = {}
@@ -251,9 +310,9 @@ def optimizer_step(groups: Sequence[MuonGroup], hp: MuonHParams, adamw_segments:
         side = _SIDE[dev] = torch.cuda.Stream(device=dev)
     garr, keep = _groups_c(groups)
     h, tab = hp.to_c()
-    arr = _adamw_c(adamw_segments)
+    arr, n_seg = _adamw_c(adamw_segments)
     L.check(L.lib().ma_muon_adamw_step(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
-                                       workspace.numel(), arr, len(adamw_segments), int(background_workgroups),
+                                       workspace.numel(), arr, n_seg, int(background_workgroups),
                                        C.c_void_p(_stream(dev)), C.c_void_p(side.cuda_stream)))
     return workspace
 

@@ -68,19 +68,6 @@ inline int64_t dt_bytes(int dt) { return dt == MA_BF16 ? 2 : 4; }
 inline bool dt_valid(int dt) { return dt == MA_F32 || dt == MA_BF16; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Newton-Schulz GEMM tiles. The symmetric products (Gram, polynomial) need
-// square tiles; MA_NS_TILE / MA_NS_TILE_SYM ("BMxBNxBK:WGMxWGN") override the
-// bf16 choices for tuning.
-NsTile parse_tile(const char* env, NsTile d) {
-  if (const char* e = getenv(env)) {
-    if (strcmp(e, "dma") == 0) return {256, 256, ns_dma_bk(), 2, 2, 1};
-    if (strcmp(e, "dma8") == 0) return {256, 256, ns_dma_bk(), 2, 4, 1};
-    NsTile x{};
-    if (sscanf(e, "%dx%dx%d:%dx%d", &x.bm, &x.bn, &x.bk, &x.wgm, &x.wgn) == 5) return x;
-  }
-  return d;
-}
-
 NsTile ns_tile(int dtype, bool symmetric);
 
 // Whether the AXPY launches read X^T from the row-major X through transposing
@@ -102,13 +89,12 @@ bool ns_b_upper(int dtype) {
 }
 
 
-NsTile ns_tile(int dtype, bool symmetric) {
+// Newton-Schulz GEMM tiles (the symmetric products need square ones): in bf16
+// the LDS-DMA kernel, 256 x 256 x 64 with 8 waves (2 x 4 of 128 x 64, two per
+// SIMD); in fp32 the register-staged kernel, 128 x 128 x 32 with 2 x 2 waves.
+NsTile ns_tile(int dtype, bool /*symmetric*/) {
   if (dtype != MA_BF16) return {128, 128, 32, 2, 2, 0};
-  // the LDS-DMA kernel with 8 waves (2 x 4 of 128 x 64, two per SIMD); "dma"
-  // selects the 4-wave form (2 x 2 of 128 x 128)
-  static const NsTile axpy = parse_tile("MA_NS_TILE", {256, 256, ns_dma_bk(), 2, 4, 1});
-  static const NsTile sym = parse_tile("MA_NS_TILE_SYM", {256, 256, ns_dma_bk(), 2, 4, 1});
-  return symmetric ? sym : axpy;
+  return {256, 256, ns_dma_bk(), 2, 4, 1};
 }
 
 // ----------------------------------------------------------------------------
@@ -123,6 +109,8 @@ struct GroupPlan {
   int64_t x_stride, a_stride, row_stride;   // elements / floats
   size_t off_x[2], off_xt[2], off_a, off_b, off_rowsq, off_rowf;   // bytes
   size_t off_part;           // update-norm partial sums: count x ppm_max x 2 floats
+  size_t off_flags;          // non-finite flags: count int32
+  bool check_finite;
   int ppm_max;
   const ma_muon_group* src;
   // views in the parameter's layout ("direct") and transposed
@@ -168,6 +156,7 @@ void plan_group(GroupPlan& p, int64_t R, int64_t C, int count, int dt_x, size_t&
   p.off_rowf = off;  off = align_up(off + (size_t)(count * p.row_stride * 4), MA_WORKSPACE_ALIGN);
   p.ppm_max = post_blocks_per_mat_max(R, C);
   p.off_part = off;  off = align_up(off + (size_t)count * p.ppm_max * 2 * 4, MA_WORKSPACE_ALIGN);
+  p.off_flags = off; off = align_up(off + (size_t)count * 4, MA_WORKSPACE_ALIGN);
 }
 
 int validate_hparams(const ma_muon_hparams* hp) {
@@ -180,6 +169,8 @@ int validate_hparams(const ma_muon_hparams* hp) {
   if (hp->lr_scale < MA_SCALE_NONE || hp->lr_scale > MA_SCALE_SQRT_MAX)
     return fail(MA_ERR_INVALID_ARG, "lr_scale %d is not an ma_scale value", hp->lr_scale);
   if (!dt_valid(hp->ns_precision)) return fail(MA_ERR_UNSUPPORTED, "ns_precision %d", hp->ns_precision);
+  if (hp->check_finite != 0 && hp->check_finite != 1)
+    return fail(MA_ERR_INVALID_ARG, "check_finite %d is not 0 or 1", hp->check_finite);
   if (!std::isfinite(hp->lr) || !std::isfinite(hp->momentum) || !std::isfinite(hp->weight_decay) ||
       !std::isfinite(hp->norm_eps) || !std::isfinite(hp->eq_eps))
     return fail(MA_ERR_INVALID_ARG, "non-finite hyperparameter");
@@ -188,15 +179,29 @@ int validate_hparams(const ma_muon_hparams* hp) {
   return MA_OK;
 }
 
+// A device buffer's byte range and what it is (for the message).
+enum RangeTag { R_PARAM, R_GRAD, R_MOMENTUM, R_WORKSPACE, R_STATS, R_ADAMW, R_LION };
 struct Range { uintptr_t lo, hi; int tag; };
+
+const char* range_name(int tag) {
+  switch (tag) {
+    case R_PARAM: return "a Muon parameter";
+    case R_GRAD: return "a Muon gradient";
+    case R_MOMENTUM: return "a Muon momentum buffer";
+    case R_WORKSPACE: return "the workspace";
+    case R_STATS: return "the stats array";
+    case R_ADAMW: return "an AdamW buffer";
+    case R_LION: return "a Lion buffer";
+  }
+  return "a buffer";
+}
 
 int check_overlaps(std::vector<Range>& rs) {
   std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
   for (size_t i = 1; i < rs.size(); ++i)
     if (rs[i].lo < rs[i - 1].hi)
-      return fail(MA_ERR_INVALID_ARG, "device buffers overlap (%s and %s)",
-                  rs[i - 1].tag == 3 ? "workspace" : "a parameter/gradient/momentum buffer",
-                  rs[i].tag == 3 ? "workspace" : "a parameter/gradient/momentum buffer");
+      return fail(MA_ERR_INVALID_ARG, "device buffers overlap (%s and %s)", range_name(rs[i - 1].tag),
+                  range_name(rs[i].tag));
   return MA_OK;
 }
 
@@ -250,6 +255,7 @@ int build_plan(const ma_muon_group* groups, int32_t n, const ma_muon_hparams* hp
     const double lr_eff = (double)hp->lr * mult;
     p.c_lr = (float)lr_eff;
     p.c_wd = (float)(lr_eff * (double)hp->weight_decay);
+    p.check_finite = hp->check_finite != 0;
     p.src = &groups[i];
     plan.g.push_back(p);
   }
@@ -296,7 +302,6 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
   a.decay = hp->weight_decay != 0.0f ? 1 : 0;
   a.norm_eps = hp->norm_eps;
   a.eq_eps = hp->eq_eps;
-  a.finalize_mode = hp->equilibrate == MA_EQ_ROWS_PRE ? 1 : 0;
   for (int i = 0; i < cnt; ++i) {
     const int k = first + i;
     a.mat[i].g = p.src ? p.src->grads[k] : nullptr;
@@ -304,6 +309,7 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
     a.mat[i].w = p.src ? p.src->params[k] : nullptr;
   }
   a.vec = group_vec(p) ? 1 : 0;
+  a.nonfinite = hp->check_finite ? reinterpret_cast<int32_t*>(ws + p.off_flags) + first : nullptr;
   return a;
 }
 
@@ -311,10 +317,9 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
 // scaled (optional): per group, whether X0 holds Y with X0 = s Y, s in the
 // group's row-factor slot of row 0 of each matrix (k_finalize mode 4).
 // before_axpy (optional): called once, before the first AXPY launch is enqueued.
-#ifndef MA_FORK_AT
-#define MA_FORK_AT 2
-#endif
-constexpr int kForkAt = MA_FORK_AT;   // 3 * step + product (GRAM 0, POLY 1, AXPY 2)
+// the AdamW fork of ma_muon_adamw_step: before product 3 * step + (GRAM 0,
+// POLY 1, AXPY 2) = the first AXPY
+constexpr int kForkAt = 2;
 int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
                hipStream_t s, const std::vector<char>* scaled = nullptr,
                const std::function<int()>* before_axpy = nullptr) {
@@ -447,6 +452,7 @@ const char* ma_status_string(int status) {
     case MA_ERR_UNSUPPORTED: return "unsupported dtype combination";
     case MA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case MA_ERR_HIP: return "HIP runtime error";
+    case MA_ERR_NONFINITE: return "non-finite values in a Muon step";
   }
   return "unknown status";
 }
@@ -511,71 +517,124 @@ bool pre_rows_for(const GroupPlan& p, const ma_muon_hparams* hp) {
 }
 
 namespace {
-// fork (optional): called once, when the first AXPY is about to be enqueued
-// (or after the last launch when there is none).
-int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
-                   size_t workspace_bytes, float* stats, void* stream,
-                   const std::function<int()>* fork = nullptr) {
-  bool forked = false;
-  std::function<int()> fork_once = [&]() -> int {
-    if (forked || !fork) return MA_OK;
-    forked = true;
-    return (*fork)();
-  };
-  Plan plan;
+// k_finalize launches batched over groups: add() queues one group's
+// matrices, flush() launches what is queued (also when a batch fills).
+struct FinalizeBatch {
+  FinalizeArgs a{};
+  int blocks = 0;
+  hipStream_t s;
+  FinalizeBatch(const ma_muon_hparams* hp, hipStream_t st) : s(st) {
+    a.norm_eps = hp->norm_eps;
+    a.eq_eps = hp->eq_eps;
+  }
+  int add(const GroupPlan& p, unsigned char* ws, int mode) {
+    if (p.count == 0) return MA_OK;
+    if (a.n == kMaxFinalizeGroups) {
+      const int rc = flush();
+      if (rc) return rc;
+    }
+    FinalizeGroup& g = a.g[a.n++];
+    g.rowsq = reinterpret_cast<const float*>(ws + p.off_rowsq);
+    g.rowf = reinterpret_cast<float*>(ws + p.off_rowf);
+    g.nonfinite = p.check_finite ? reinterpret_cast<int32_t*>(ws + p.off_flags) : nullptr;
+    g.row_stride = p.row_stride;
+    g.R = (int32_t)p.R;
+    g.C = (int32_t)p.C;
+    g.mode = mode;
+    g.block_begin = blocks;
+    blocks += p.count;
+    return MA_OK;
+  }
+  int flush() {
+    if (a.n == 0) return MA_OK;
+    hipError_t err;
+    {
+      ProfScope ps(MA_K_FINALIZE, s);
+      err = launch_finalize(a, blocks, s);
+    }
+    a.n = 0;
+    blocks = 0;
+    return err == hipSuccess ? MA_OK : hip_fail(err, "norm finalize");
+  }
+};
+
+// Everything a Muon call checks before its first launch (no HIP call): the
+// plan, the workspace, and the byte range of every device buffer it touches,
+// appended to `rs` for the overlap check.
+// caller_ws false: the workspace is not the caller's (not checked, not in
+// `rs`).
+int muon_prepare(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
+                 size_t workspace_bytes, float* stats, Plan& plan, std::vector<Range>& rs, bool caller_ws = true) {
   int rc = build_plan(groups, n_groups, hp, plan, true);
   if (rc) return rc;
   int64_t total = 0;
   for (const GroupPlan& p : plan.g) total += p.count;
-  if (plan.bytes > 0) {
+  if (caller_ws && plan.bytes > 0) {
     if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is null");
     if ((uintptr_t)workspace % MA_WORKSPACE_ALIGN)
       return fail(MA_ERR_WORKSPACE, "workspace is not %d-byte aligned", MA_WORKSPACE_ALIGN);
     if (workspace_bytes < plan.bytes)
       return fail(MA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.bytes);
   }
-  // no two buffers may overlap (including the workspace)
-  std::vector<Range> rs;
   for (const GroupPlan& p : plan.g) {
     const ma_muon_group& g = *p.src;
     const uintptr_t ne = (uintptr_t)(p.R * p.C);
     for (int i = 0; i < g.count; ++i) {
-      rs.push_back({(uintptr_t)g.params[i], (uintptr_t)g.params[i] + ne * dt_bytes(p.dt_p), 0});
-      rs.push_back({(uintptr_t)g.grads[i], (uintptr_t)g.grads[i] + ne * dt_bytes(p.dt_g), 1});
-      rs.push_back({(uintptr_t)g.momentum[i], (uintptr_t)g.momentum[i] + ne * dt_bytes(p.dt_m), 2});
+      rs.push_back({(uintptr_t)g.params[i], (uintptr_t)g.params[i] + ne * dt_bytes(p.dt_p), R_PARAM});
+      rs.push_back({(uintptr_t)g.grads[i], (uintptr_t)g.grads[i] + ne * dt_bytes(p.dt_g), R_GRAD});
+      rs.push_back({(uintptr_t)g.momentum[i], (uintptr_t)g.momentum[i] + ne * dt_bytes(p.dt_m), R_MOMENTUM});
     }
   }
-  if (plan.bytes > 0) rs.push_back({(uintptr_t)workspace, (uintptr_t)workspace + plan.bytes, 3});
-  if (stats && total > 0) rs.push_back({(uintptr_t)stats, (uintptr_t)(stats + 2 * total), 3});
-  rc = check_overlaps(rs);
-  if (rc) return rc;
+  if (caller_ws && plan.bytes > 0) rs.push_back({(uintptr_t)workspace, (uintptr_t)workspace + plan.bytes, R_WORKSPACE});
+  if (stats && total > 0) rs.push_back({(uintptr_t)stats, (uintptr_t)(stats + 2 * total), R_STATS});
+  return MA_OK;
+}
 
+// The launches of a Muon call that muon_prepare accepted. fork (optional):
+// called once, when the first AXPY is about to be enqueued (or after the last
+// launch when there is none).
+int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, float* stats, void* stream,
+                 const std::function<int()>* fork = nullptr) {
+  bool forked = false;
+  std::function<int()> fork_once = [&]() -> int {
+    if (forked || !fork) return MA_OK;
+    forked = true;
+    return (*fork)();
+  };
+  int rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   hipError_t err;
-  // 1. norms, 2. factors, 3. momentum update and X0 (both layouts); or the
-  // row pass (momentum, norms, row-scaled X0) and the Frobenius factor alone
+  // 1. per group: the row pass (momentum, row sums and the row-scaled X0), or
+  // the row sums alone; 2. one launch of the per-matrix factors for every
+  // group; 3. per two-pass group: the momentum update and X0
   std::vector<char> scaled(plan.g.size(), 0);
+  FinalizeBatch fin(hp, s);
   for (size_t gi = 0; gi < plan.g.size(); ++gi) {
     const GroupPlan& p = plan.g[gi];
+    if (p.count == 0) continue;
+    scaled[gi] = pre_rows_for(p, hp) ? 1 : 0;
     for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
       const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
-      ElemArgs a = elem_args(p, hp, ws, first, cnt);
-      if (first == 0) scaled[gi] = pre_rows_for(p, hp) ? 1 : 0;
+      const ElemArgs a = elem_args(p, hp, ws, first, cnt);
       if (scaled[gi]) {
         // a.xd is X0 in the parameter's layout, which is the iteration's
         { ProfScope ps(MA_K_PRE, s); err = launch_pre_rows(p.dt_g, p.dt_m, p.dt_x, a, s); }
         if (err != hipSuccess) return hip_fail(err, "momentum/row norms/X0");
-        a.finalize_mode = 4;
-        { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
-        if (err != hipSuccess) return hip_fail(err, "norm finalize");
-        continue;
+      } else {
+        { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_momentum(p.dt_g, p.dt_m, a, s); }
+        if (err != hipSuccess) return hip_fail(err, "row norms");
       }
-      { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_momentum(p.dt_g, p.dt_m, a, s); }
-      if (err != hipSuccess) return hip_fail(err, "row norms");
-      { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
-      if (err != hipSuccess) return hip_fail(err, "norm finalize");
-      ElemArgs ap = a;
+    }
+    if ((rc = fin.add(p, ws, scaled[gi] ? 4 : (hp->equilibrate == MA_EQ_ROWS_PRE ? 1 : 0)))) return rc;
+  }
+  if ((rc = fin.flush())) return rc;
+  for (size_t gi = 0; gi < plan.g.size(); ++gi) {
+    const GroupPlan& p = plan.g[gi];
+    if (scaled[gi]) continue;
+    for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
+      const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
+      ElemArgs ap = elem_args(p, hp, ws, first, cnt);
       if (ns_q_transposed(p.dt_x)) {
         // X0 in the iteration's layout X (for T > 0) and in the parameter's
         // layout (for T = 0); X0^T is not needed
@@ -590,24 +649,34 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
   // 4. T quintic steps
   rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s, &scaled, &fork_once);
   if (rc) return rc;
-  // 5. (MuonEq POST) and the update (and the update norms)
+  // 5. (MuonEq POST, NorMuon: the update's row sums, one launch of the row
+  // factors) and the update (and the update norms)
   const int ub = hp->ns_steps & 1;
+  const bool rows_after = hp->equilibrate == MA_EQ_ROWS_POST || hp->equilibrate == MA_EQ_ROWS_RMS;
+  auto update_args = [&](const GroupPlan& p, int first, int cnt) {
+    ElemArgs a = elem_args(p, hp, ws, first, cnt);
+    a.xd = ws + p.off_direct(ub) + (size_t)(first * p.x_stride * dt_bytes(p.dt_x));
+    a.xt = nullptr;
+    if (!rows_after) a.rowf = nullptr;
+    return a;
+  };
+  if (rows_after) {
+    for (const GroupPlan& p : plan.g) {
+      if (p.count == 0) continue;
+      for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
+        const ElemArgs a = update_args(p, first, std::min(kMaxMatsPerLaunch, p.count - first));
+        { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_buffer(p.dt_x, a, s); }
+        if (err != hipSuccess) return hip_fail(err, "update row norms");
+      }
+      if ((rc = fin.add(p, ws, hp->equilibrate == MA_EQ_ROWS_POST ? 2 : 3))) return rc;
+    }
+    if ((rc = fin.flush())) return rc;
+  }
   int64_t mat0 = 0;   // index of the group's first matrix in `stats`
   for (const GroupPlan& p : plan.g) {
     for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
       const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
-      ElemArgs a = elem_args(p, hp, ws, first, cnt);
-      a.xd = ws + p.off_direct(ub) + (size_t)(first * p.x_stride * dt_bytes(p.dt_x));
-      a.xt = nullptr;
-      if (hp->equilibrate == MA_EQ_ROWS_POST || hp->equilibrate == MA_EQ_ROWS_RMS) {
-        a.finalize_mode = hp->equilibrate == MA_EQ_ROWS_POST ? 2 : 3;
-        { ProfScope ps(MA_K_ROWNORM, s); err = launch_rowsumsq_buffer(p.dt_x, a, s); }
-        if (err != hipSuccess) return hip_fail(err, "update row norms");
-        { ProfScope ps(MA_K_FINALIZE, s); err = launch_finalize(a, s); }
-        if (err != hipSuccess) return hip_fail(err, "update row factors");
-      } else {
-        a.rowf = nullptr;
-      }
+      ElemArgs a = update_args(p, first, cnt);
       a.tiles_r = (int32_t)((p.R + 63) / 64);
       a.tiles_c = (int32_t)((p.C + 63) / 64);
       const int ppm = post_blocks_per_mat(a);   // <= p.ppm_max
@@ -623,6 +692,16 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
   }
   return fork_once();
 }
+
+int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
+                   size_t workspace_bytes, float* stats, void* stream) {
+  Plan plan;
+  std::vector<Range> rs;
+  int rc = muon_prepare(groups, n_groups, hp, workspace, workspace_bytes, stats, plan, rs);
+  if (rc) return rc;
+  if ((rc = check_overlaps(rs))) return rc;   // no two buffers may overlap, workspace included
+  return muon_enqueue(plan, hp, workspace, stats, stream);
+}
 }  // namespace
 
 int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
@@ -634,6 +713,30 @@ int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_m
                        void* workspace, size_t workspace_bytes, float* stats, void* stream) {
   if (!stats || ((uintptr_t)stats & 3)) return fail(MA_ERR_INVALID_ARG, "stats is null or not 4-byte aligned");
   return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, stats, stream);
+}
+
+int ma_muon_nonfinite(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                      const void* workspace, int32_t* flags) {
+  Plan plan;
+  int rc = build_plan(groups, n_groups, hp, plan, false);
+  if (rc) return rc;
+  if (!hp->check_finite) return fail(MA_ERR_INVALID_ARG, "the step was not asked to check (check_finite == 0)");
+  if (!workspace) return fail(MA_ERR_WORKSPACE, "workspace is null");
+  std::vector<int32_t> f;
+  bool any = false;
+  for (const GroupPlan& p : plan.g) {
+    if (p.count == 0) continue;
+    const size_t at = f.size();
+    f.resize(at + p.count);
+    const hipError_t err = hipMemcpy(f.data() + at, reinterpret_cast<const unsigned char*>(workspace) + p.off_flags,
+                                     (size_t)p.count * 4, hipMemcpyDeviceToHost);
+    if (err != hipSuccess) return hip_fail(err, "reading the non-finite flags");
+  }
+  for (size_t i = 0; i < f.size(); ++i) {
+    any = any || f[i] != 0;
+    if (flags) flags[i] = f[i] != 0 ? 1 : 0;
+  }
+  return any ? fail(MA_ERR_NONFINITE, "a Muon matrix had non-finite norms; its weight was left unchanged") : MA_OK;
 }
 
 int ma_muon_row_pass(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, int32_t group) {
@@ -664,9 +767,10 @@ int ma_muon_workspace_update(const ma_muon_group* groups, int32_t n_groups, cons
 }
 
 namespace {
-int adamw_validate(const ma_adamw_segment* segs, int32_t n) {
+// Argument checks of an AdamW call (no HIP call); the buffers' byte ranges
+// are appended to `rs` for the overlap check.
+int adamw_prepare(const ma_adamw_segment* segs, int32_t n, std::vector<Range>& rs) {
   if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
-  std::vector<Range> rs;
   for (int i = 0; i < n; ++i) {
     const ma_adamw_segment& S = segs[i];
     if (S.n < 0) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0", i);
@@ -682,12 +786,18 @@ int adamw_validate(const ma_adamw_segment* segs, int32_t n) {
         !std::isfinite(S.weight_decay) || S.beta1 < 0.f || S.beta1 >= 1.f || S.beta2 < 0.f || S.beta2 >= 1.f)
       return fail(MA_ERR_INVALID_ARG, "segment %d: hyperparameters out of range", i);
     const uintptr_t nb = (uintptr_t)S.n * 4;
-    rs.push_back({(uintptr_t)S.param, (uintptr_t)S.param + nb, 0});
-    rs.push_back({(uintptr_t)S.grad, (uintptr_t)S.grad + nb, 1});
-    rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, 2});
-    rs.push_back({(uintptr_t)S.exp_avg_sq, (uintptr_t)S.exp_avg_sq + nb, 2});
+    rs.push_back({(uintptr_t)S.param, (uintptr_t)S.param + nb, R_ADAMW});
+    rs.push_back({(uintptr_t)S.grad, (uintptr_t)S.grad + nb, R_ADAMW});
+    rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, R_ADAMW});
+    rs.push_back({(uintptr_t)S.exp_avg_sq, (uintptr_t)S.exp_avg_sq + nb, R_ADAMW});
   }
-  return check_overlaps(rs);
+  return MA_OK;
+}
+
+int adamw_validate(const ma_adamw_segment* segs, int32_t n) {
+  std::vector<Range> rs;
+  const int rc = adamw_prepare(segs, n, rs);
+  return rc ? rc : check_overlaps(rs);
 }
 
 // Launches for segments that adamw_validate accepted.
@@ -765,6 +875,10 @@ int fork_events(hipEvent_t& e_fork, hipEvent_t& e_join) {
   e_join = it->second.second;
   return MA_OK;
 }
+
+// Test hook (ma_test_fail_after_fork): the calling thread's next
+// ma_muon_adamw_step fails right after its fork, as a launch error there would.
+thread_local bool g_fail_after_fork = false;
 }  // namespace
 
 int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
@@ -772,26 +886,46 @@ int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_m
                        int32_t workgroups, void* stream, void* side_stream) {
   if (workgroups < 1) return fail(MA_ERR_INVALID_ARG, "workgroups must be >= 1");
   if (side_stream == stream) return fail(MA_ERR_INVALID_ARG, "side_stream must differ from stream");
-  int rc = adamw_validate(segs, n_segs);
+  // every argument of both steps, and one overlap check over the buffers of
+  // both (they run concurrently), before anything is enqueued
+  Plan plan;
+  std::vector<Range> rs;
+  int rc = muon_prepare(groups, n_groups, hp, workspace, workspace_bytes, nullptr, plan, rs);
   if (rc) return rc;
+  if ((rc = adamw_prepare(segs, n_segs, rs))) return rc;
+  if ((rc = check_overlaps(rs))) return rc;
+  const bool inject = g_fail_after_fork;
+  g_fail_after_fork = false;
   hipEvent_t e_fork = nullptr, e_join = nullptr;
   if ((rc = fork_events(e_fork, e_join))) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream), side = reinterpret_cast<hipStream_t>(side_stream);
   // AdamW joins once the Muon step's elementwise passes and first GRAM and
   // POLY are done: it then runs beside the AXPY and later products
+  bool side_waits = false;   // the side stream has work ordered after the fork
   std::function<int()> fork = [&]() -> int {
     hipError_t err;
     if ((err = hipEventRecord(e_fork, s)) != hipSuccess) return hip_fail(err, "fork record");
     if ((err = hipStreamWaitEvent(side, e_fork, 0)) != hipSuccess) return hip_fail(err, "fork wait");
+    side_waits = true;
     const int r = adamw_enqueue(segs, n_segs, workgroups, side_stream);
-    if (r) return r;
-    if ((err = hipEventRecord(e_join, side)) != hipSuccess) return hip_fail(err, "join record");
-    return MA_OK;
+    if (r == MA_OK && inject) return fail(MA_ERR_HIP, "failure injected after the fork (test hook)");
+    return r;
   };
-  rc = muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, nullptr, stream, &fork);
-  if (rc) return rc;
-  const hipError_t err = hipStreamWaitEvent(s, e_join, 0);
-  return err == hipSuccess ? MA_OK : hip_fail(err, "join wait");
+  rc = muon_enqueue(plan, hp, workspace, nullptr, stream, &fork);
+  if (side_waits) {
+    // the join, on every path once the side stream waits on the fork: the
+    // caller's stream must not run ahead of AdamW work already queued, and a
+    // graph capture must not end with the side stream unjoined
+    hipError_t err = hipEventRecord(e_join, side);
+    if (err == hipSuccess) err = hipStreamWaitEvent(s, e_join, 0);
+    if (err != hipSuccess && rc == MA_OK) rc = hip_fail(err, "join");
+  }
+  return rc;
+}
+
+int ma_test_fail_after_fork(void) {
+  g_fail_after_fork = true;
+  return MA_OK;
 }
 
 int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
@@ -819,9 +953,9 @@ int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {
         !(S.beta2 >= 0.f && S.beta2 < 1.f))
       return fail(MA_ERR_INVALID_ARG, "segment %d: hyperparameters out of range", i);
     const uintptr_t nb = (uintptr_t)S.n * 4;
-    rs.push_back({(uintptr_t)S.param, (uintptr_t)S.param + nb, 0});
-    rs.push_back({(uintptr_t)S.grad, (uintptr_t)S.grad + nb, 1});
-    rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, 2});
+    rs.push_back({(uintptr_t)S.param, (uintptr_t)S.param + nb, R_LION});
+    rs.push_back({(uintptr_t)S.grad, (uintptr_t)S.grad + nb, R_LION});
+    rs.push_back({(uintptr_t)S.exp_avg, (uintptr_t)S.exp_avg + nb, R_LION});
   }
   int rc = check_overlaps(rs);
   if (rc) return rc;

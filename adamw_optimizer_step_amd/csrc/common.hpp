@@ -77,12 +77,8 @@ __device__ __forceinline__ void st16f(void* p, const float4& x) {
   st16<NT>(p, make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)));
 }
 
-// Non-temporal access in the Muon elementwise kernels (build with -DMA_NT=0
-// to compare against cached access).
-#ifndef MA_NT
-#define MA_NT 1
-#endif
-constexpr bool kNT = MA_NT != 0;
+// Non-temporal access for the data the Muon elementwise kernels touch once.
+constexpr bool kNT = true;
 
 // load / store n consecutive elements of storage type DT as fp32 (n = 8: one
 // 16-byte vector for bf16, two for fp32). Pointers must be 16-byte aligned.

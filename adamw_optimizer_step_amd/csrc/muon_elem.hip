@@ -164,21 +164,25 @@ __global__ void __launch_bounds__(256) k_rowsumsq_buffer(const ElemArgs a) {
   }
 }
 
-// One block per matrix; fixed-order reduction (strided partial sums, then an
-// LDS tree), so results do not depend on scheduling.
-__global__ void __launch_bounds__(256) k_finalize(const ElemArgs a) {
+// One block per matrix, every group of the launch (a group's matrices are
+// blocks g.block_begin ..); fixed-order reduction (strided partial sums, then
+// an LDS tree), so results do not depend on scheduling.
+__global__ void __launch_bounds__(256) k_finalize(const FinalizeArgs fa) {
   __shared__ float red[256];
-  const int k = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < fa.n && (int)blockIdx.x >= fa.g[gi + 1].block_begin) ++gi;
+  const FinalizeGroup& a = fa.g[gi];
+  const int k = (int)blockIdx.x - a.block_begin;
   const float* rs = a.rowsq + (int64_t)k * a.row_stride;
   float* rf = a.rowf + (int64_t)k * a.row_stride;
   const int t = threadIdx.x;
-  const int mode = a.finalize_mode;
+  const int mode = a.mode;
   float part = 0.0f;
   for (int i = t; i < a.R; i += 256) {
     const float q = rs[i];
     if (mode == 1 || mode == 4) {
       const float n = sqrtf(q);
-      const float y = n / (n + a.eq_eps);   // norm of the equilibrated row
+      const float y = n / (n + fa.eq_eps);   // norm of the equilibrated row
       part += y * y;
     } else {
       part += q;
@@ -191,23 +195,29 @@ __global__ void __launch_bounds__(256) k_finalize(const ElemArgs a) {
     __syncthreads();
   }
   const float total = red[0];
+  if (a.nonfinite && t == 0) {
+    // a non-finite entry (or an overflowing square) makes the sum non-finite
+    const bool bad = !__builtin_isfinite(total);
+    if (mode == 0 || mode == 1 || mode == 4) a.nonfinite[k] = bad ? 1 : 0;
+    else if (bad) a.nonfinite[k] = 1;
+  }
   if (mode == 0) {
-    const float s = 1.0f / (sqrtf(total) + a.norm_eps);
+    const float s = 1.0f / (sqrtf(total) + fa.norm_eps);
     for (int i = t; i < a.R; i += 256) rf[i] = s;
   } else if (mode == 1) {
-    const float s = 1.0f / (sqrtf(total) + a.norm_eps);
-    for (int i = t; i < a.R; i += 256) rf[i] = s / (sqrtf(rs[i]) + a.eq_eps);
+    const float s = 1.0f / (sqrtf(total) + fa.norm_eps);
+    for (int i = t; i < a.R; i += 256) rf[i] = s / (sqrtf(rs[i]) + fa.eq_eps);
   } else if (mode == 4) {
     // MuonEq pre with the row factors already applied (k_pre_rows): only the
     // matrix's Frobenius factor, in the row-factor slot of row 0
-    if (t == 0) rf[0] = 1.0f / (sqrtf(total) + a.norm_eps);
+    if (t == 0) rf[0] = 1.0f / (sqrtf(total) + fa.norm_eps);
   } else if (mode == 2) {
     const float rho = sqrtf(total) / sqrtf((float)a.R);
-    for (int i = t; i < a.R; i += 256) rf[i] = rho / (sqrtf(rs[i]) + a.eq_eps);
+    for (int i = t; i < a.R; i += 256) rf[i] = rho / (sqrtf(rs[i]) + fa.eq_eps);
   } else {
     // row RMS: ||U_i|| / sqrt(cols)
     const float sc = sqrtf((float)a.C);
-    for (int i = t; i < a.R; i += 256) rf[i] = 1.0f / (sqrtf(rs[i]) / sc + a.eq_eps);
+    for (int i = t; i < a.R; i += 256) rf[i] = 1.0f / (sqrtf(rs[i]) / sc + fa.eq_eps);
   }
 }
 
@@ -415,6 +425,9 @@ __device__ __forceinline__ void post_vec_body(const ElemArgs& a, int blocks_per_
   const void* xd = eptr<DTX>(static_cast<const void*>(a.xd), (int64_t)k * a.x_stride);
   const float* rowf = a.rowf ? a.rowf + (int64_t)k * a.row_stride : nullptr;
   const uint32_t step = (uint32_t)blocks_per_mat * 256u;
+  // a matrix flagged non-finite keeps its weight (the sums still see W)
+  const bool keep = a.nonfinite && a.nonfinite[k];
+  if (keep && !STATS) return;
   float sd = 0.0f, sw = 0.0f;   // sums of (W' - W)^2 and W^2 (stored values)
   for (uint32_t q0 = (uint32_t)b * 256u + threadIdx.x; q0 < nch; q0 += step * kPostChunks) {
     float w[kPostChunks][8], u[kPostChunks][8];
@@ -436,10 +449,10 @@ __device__ __forceinline__ void post_vec_body(const ElemArgs& a, int blocks_per_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float w0 = w[v][e];
-          w[v][e] = post_elem(w0, u[v][e], f, rowf != nullptr, a);
+          w[v][e] = keep ? w0 : post_elem(w0, u[v][e], f, rowf != nullptr, a);
           if constexpr (STATS) update_sums<DTP>(w0, w[v][e], sd, sw);
         }
-        store8<DTP, kNT>(eptr<DTP>(wp, (int64_t)rr[v] * a.C + cc[v]), w[v]);
+        if (!keep) store8<DTP, kNT>(eptr<DTP>(wp, (int64_t)rr[v] * a.C + cc[v]), w[v]);
       }
     }
   }
@@ -468,6 +481,8 @@ __device__ __forceinline__ void post_tile_body(const ElemArgs& a) {
   const int tid = threadIdx.x;
   const int cl = (tid & 7) * 8;
   const bool vec = a.vec && (a.ld_d & 7) == 0;
+  const bool keep = a.nonfinite && a.nonfinite[k];   // flagged: the weight stays
+  if (keep && !STATS) return;
   float sd = 0.0f, sw = 0.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -491,9 +506,10 @@ __device__ __forceinline__ void post_tile_body(const ElemArgs& a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float w0 = w[e];
-      w[e] = post_elem(w0, u[e], f, a.rowf != nullptr, a);
+      w[e] = keep ? w0 : post_elem(w0, u[e], f, a.rowf != nullptr, a);
       if (STATS && e < n) update_sums<DTP>(w0, w[e], sd, sw);
     }
+    if (keep) continue;
     if (vec) {
       store8<DTP>(eptr<DTP>(wp, off), w);
     } else {
@@ -584,9 +600,9 @@ hipError_t launch_rowsumsq_buffer(int dt_x, const ElemArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const ElemArgs& a, hipStream_t s) {
-  if (a.count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_finalize, dim3(a.count), dim3(256), 0, s, a);
+hipError_t launch_finalize(const FinalizeArgs& a, int blocks, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_finalize, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

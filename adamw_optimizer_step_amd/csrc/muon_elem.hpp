@@ -28,18 +28,40 @@ struct ElemArgs {
   float c_lr, c_wd;
   int32_t cautious, decay;
   float norm_eps, eq_eps;
-  int32_t finalize_mode;     // 0: Frobenius only, 1: MuonEq pre, 2: MuonEq post, 3: row RMS,
-                             // 4: MuonEq pre, Frobenius factor only (into rowf[0])
   int32_t vec;               // C % 8 == 0 and every matrix pointer 16-byte aligned
   int32_t pure_copy;         // k_pre: X0 = G (no momentum; M untouched)
   float* part;               // k_post: per-block (sum (W'-W)^2, sum W^2), 2 floats per block, or null
+  // per-matrix non-finite flags (matrix k at nonfinite[k]) or null (no check):
+  // k_finalize sets a matrix's flag when its sums of squares are not finite
+  // (modes 0, 1, 4 write it, modes 2, 3 only raise it); k_post then leaves
+  // that matrix's weight as it was
+  int32_t* nonfinite;
   MatPtr mat[kMaxMatsPerLaunch];
+};
+
+// k_finalize over several groups in one launch: one block per matrix, group
+// g's matrices at blocks block_begin .. (increasing over the groups).
+constexpr int kMaxFinalizeGroups = 16;
+struct FinalizeGroup {
+  const float* rowsq;        // matrix k's row sums of squares at k*row_stride
+  float* rowf;               // matrix k's factors at k*row_stride
+  int32_t* nonfinite;        // matrix k's flag at nonfinite[k], or null
+  int64_t row_stride;
+  int32_t R, C, block_begin;
+  // 0: Frobenius only, 1: MuonEq pre, 2: MuonEq post, 3: row RMS,
+  // 4: MuonEq pre, Frobenius factor only (into rowf[0])
+  int32_t mode;
+};
+struct FinalizeArgs {
+  int32_t n;
+  float norm_eps, eq_eps;
+  FinalizeGroup g[kMaxFinalizeGroups];
 };
 
 // dtype codes: DT_F32 / DT_BF16
 hipError_t launch_rowsumsq_momentum(int dt_g, int dt_m, const ElemArgs& a, hipStream_t s);
 hipError_t launch_rowsumsq_buffer(int dt_x, const ElemArgs& a, hipStream_t s);
-hipError_t launch_finalize(const ElemArgs& a, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, int blocks, hipStream_t s);
 hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s);
 // k_pre_rows (momentum, row sums and the row-scaled X0 in one pass; the
 // Frobenius factor left to the iteration) for matrices whose iteration layout

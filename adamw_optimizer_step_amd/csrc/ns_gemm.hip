@@ -18,16 +18,14 @@
 //
 // Two kernels share the job mapping and the epilogue:
 //  * ns_gemm_dma (bf16): 256 x 256 block tile, 8 waves of 128 x 64, two per
-//    SIMD (32x32x16 MFMAs, 8 accumulator blocks per wave; a 4-wave form of
-//    128 x 128 is built too). Operand tiles of 256 x 64 move from global
+//    SIMD (32x32x16 MFMAs, 8 accumulator blocks per wave). Operand tiles of 256 x 64 move from global
 //    memory straight into a 2-stage LDS ring with global_load_lds_dwordx4 (no
 //    VGPR staging), one tile ahead of the one being multiplied; 16-byte chunks
 //    are XOR-swizzled by row so that the fragment reads are conflict-free.
 //    Blocks are persistent, one per CU, each walking a fixed share of its
 //    XCD's tile list.
-//  * ns_gemm_reg (fp32; bf16 only through the tile override of the host
-//    plan): a register-staged double-buffered kernel of configurable tile and
-//    wave layout.
+//  * ns_gemm_reg (fp32): a register-staged double-buffered kernel,
+//    128 x 128 x 32 tiles of 2 x 2 waves on 32x32x2 fp32 MFMAs.
 // Blocks are dealt to the 8 XCDs so that each XCD gets an eighth of every
 // shape group, whole matrices at a time where possible (see NsArgs).
 #include "ns_gemm.hpp"
@@ -482,14 +480,8 @@ ns_gemm_reg(const NsArgs args) {
 // that one wave's fragment reads and waits overlap the other's MFMAs), a ring
 // of STAGES k-tiles in LDS
 // ---------------------------------------------------------------------------
-#ifndef MA_DMA_BK
-#define MA_DMA_BK 64
-#endif
-#ifndef MA_DMA_STAGES
-#define MA_DMA_STAGES (MA_DMA_BK == 64 ? 2 : 3)
-#endif
 namespace dma {
-constexpr int BM = 256, BN = 256, BK = MA_DMA_BK, STAGES = MA_DMA_STAGES;
+constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;
 constexpr int ROWB = BK * 2;                      // bytes per tile row
 constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
 constexpr int RPI = 1024 / ROWB;                  // rows per 1 KiB DMA instruction
@@ -498,7 +490,7 @@ constexpr int STAGE_BYTES = (BM + BN) * ROWB;     // P rows 0..255, Q rows 256..
 constexpr int MAIN = STAGES * STAGE_BYTES;
 constexpr int EPI = EpiSmem<DT_BF16, BM, BN>::BYTES;
 constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
-static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
+static_assert(BK == 64 && KK == 4, "k-tiles of 64: four MFMA k-steps");
 static_assert(STAGES >= 2 && BYTES <= 160 * 1024, "LDS ring must fit in 160 KiB");
 // per wave-grid sizes: wave sub-tile WTM x WTN of FM x FN 32x32 blocks; each
 // wave fills PANEL consecutive stage rows with DPW 1 KiB DMA instructions
@@ -814,10 +806,8 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
                                           u32x4_t (&f1a)[dma::Grid<WGM, WGN>::FM], u32x4_t (&f1b)[dma::Grid<WGM, WGN>::FN]) {
   dma_kstep<0, IIB, WGM, WGN, QT, PT>(c, kt, acc, f0a, f0b, f1a, f1b);
   dma_kstep<1, IIB, WGM, WGN, QT, PT>(c, kt, acc, f1a, f1b, f0a, f0b);
-  if constexpr (dma::KK == 4) {
-    dma_kstep<2, IIB, WGM, WGN, QT, PT>(c, kt, acc, f0a, f0b, f1a, f1b);
-    dma_kstep<3, IIB, WGM, WGN, QT, PT>(c, kt, acc, f1a, f1b, f0a, f0b);
-  }
+  dma_kstep<2, IIB, WGM, WGN, QT, PT>(c, kt, acc, f0a, f0b, f1a, f1b);
+  dma_kstep<3, IIB, WGM, WGN, QT, PT>(c, kt, acc, f1a, f1b, f0a, f0b);
 }
 
 // One output tile: prologue DMA, main loop, epilogue.
@@ -953,15 +943,8 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
     // term: Q rows j hold X^T[j][k] = X[k][j], or A[j][k] = A[k][j]
     const int e_first = (J.bi * BM + c.wm * Gd::WTM) / BK;
     for (; kt < e_first; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
-    if constexpr (BK == 32) {
-      dma_ktile<0, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<1, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<2, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<3, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
-    } else {
-      dma_ktile<0, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
-      dma_ktile<2, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
-    }
+    dma_ktile<0, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
+    dma_ktile<2, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
@@ -1035,7 +1018,7 @@ static hipError_t launch_dma_epi(int epi, bool qt, const NsArgs& a, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-#define MA_NS_TILE(BM_, BN_, BK_, WGM_, WGN_)                                                      \
+#define MA_REG_TILE(BM_, BN_, BK_, WGM_, WGN_)                                                      \
   if (tile.bm == BM_ && tile.bn == BN_ && tile.bk == BK_ && tile.wgm == WGM_ && tile.wgn == WGN_) \
     return launch_reg_epi<DTv, BM_, BN_, BK_, WGM_, WGN_>(epi, a, s);
 
@@ -1044,20 +1027,16 @@ int ns_dma_bk() { return dma::BK; }
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipStream_t s) {
   if (a.padded_blocks <= 0) return hipSuccess;
   if (dtype == DT_BF16) {
-    if (tile.dma) {
-      if (tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK) return hipErrorInvalidValue;
-      if (tile.wgm == 2 && tile.wgn == 2) return launch_dma_epi<2, 2>(epi, tile.qt != 0, a, s);
-      if (tile.wgm == 2 && tile.wgn == 4) return launch_dma_epi<2, 4>(epi, tile.qt != 0, a, s);
+    // the LDS-DMA kernel, 256 x 256 x 64 tiles, 2 x 4 waves
+    if (!tile.dma || tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK || tile.wgm != 2 || tile.wgn != 4)
       return hipErrorInvalidValue;
-    }
-    constexpr int DTv = DT_BF16;
-    MA_NS_TILE(128, 128, 64, 2, 2)
+    return launch_dma_epi<2, 4>(epi, tile.qt != 0, a, s);
   } else {
     constexpr int DTv = DT_F32;
-    MA_NS_TILE(128, 128, 32, 2, 2)
+    MA_REG_TILE(128, 128, 32, 2, 2)
   }
   return hipErrorInvalidValue;
 }
-#undef MA_NS_TILE
+#undef MA_REG_TILE
 
 }  // namespace ma

@@ -54,6 +54,8 @@ extern "C" {
 #define MA_ERR_UNSUPPORTED -2   /* dtype combination not provided */
 #define MA_ERR_WORKSPACE -3     /* workspace null, too small or misaligned */
 #define MA_ERR_HIP -4           /* a HIP runtime call or launch failed */
+#define MA_ERR_NONFINITE -5     /* ma_muon_nonfinite: a matrix of the last step had
+                                   non-finite norms (check_finite == 1 only) */
 
 typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
 
@@ -114,13 +116,25 @@ typedef struct {
  *   lr_scale      ma_scale
  *   norm_eps      added to the Frobenius norm (the pages use 1e-7)
  *   eq_eps        added to each row norm by MuonEq (1e-7), or to each row RMS
- *                 by ROWS_RMS */
+ *                 by ROWS_RMS
+ *   check_finite  1: detect non-finite values, after the fast-fail rule of
+ *                 "Chapter 4", section "Fast-Fail on NaN or Loss > 100".
+ *                 A matrix whose look-ahead momentum has a non-finite sum of
+ *                 squares (a NaN or Inf entry, or an overflowing square) --
+ *                 or, with ROWS_POST / ROWS_RMS, whose orthogonalised update
+ *                 has one -- keeps its weight unchanged (no decay, no
+ *                 update); its momentum buffer is updated as usual and holds
+ *                 the non-finite values. Every other matrix is stepped
+ *                 exactly as without the check. ma_muon_nonfinite reports
+ *                 which matrices were flagged. 0: no check (non-finite
+ *                 values propagate into the weights). */
 typedef struct {
   float lr, momentum, weight_decay;
   int32_t nesterov, ns_steps;
   const float* abc;
   int32_t cautious, equilibrate, ns_precision, lr_scale;
   float norm_eps, eq_eps;
+  int32_t check_finite;
 } ma_muon_hparams;
 
 #define MA_MAX_NS_STEPS 16
@@ -172,6 +186,17 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
  * The update itself is identical to ma_muon_step's. */
 int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                        void* workspace, size_t workspace_bytes, float* stats, void* stream);
+
+/* After a ma_muon_step / ma_muon_step_stats / ma_muon_adamw_step with
+ * check_finite == 1 has completed (the caller has synchronised its stream),
+ * the matrices it flagged: flags (HOST array of the total matrix count,
+ * groups in order, or null) receives 1 for a flagged matrix and 0 otherwise.
+ * groups, n_groups, hp and workspace must be those of the step. Returns MA_OK
+ * when no matrix was flagged, MA_ERR_NONFINITE when one was, or
+ * MA_ERR_INVALID_ARG when hp->check_finite is 0 (the step wrote no flags).
+ * Synchronous: it copies the flags from device memory. */
+int ma_muon_nonfinite(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
+                      const void* workspace, int32_t* flags);
 
 /* Whether ma_muon_step treats group `group` in one pass over G and M: the
  * momentum update, MuonEq PRE's row sums and the row-scaled X0 together, the
@@ -242,8 +267,11 @@ int ma_adamw_step_background(const ma_adamw_segment* segments, int32_t n_segment
  * ma_adamw_step. side_stream must differ from stream (both may be captured
  * into one HIP graph: the fork and join are event records and waits on
  * events the library creates once per device and host thread). Every
- * argument is validated before the first launch; Muon and AdamW buffers must
- * not overlap. */
+ * argument is validated before the first launch, and no two buffers of the
+ * two steps (Muon parameters, gradients, momentum, the workspace, AdamW
+ * buffers) may overlap (MA_ERR_INVALID_ARG). If a launch fails after the
+ * fork, `stream` still waits for what was queued on side_stream before the
+ * error is returned. */
 int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                        void* workspace, size_t workspace_bytes, const ma_adamw_segment* segments,
                        int32_t n_segments, int32_t workgroups, void* stream, void* side_stream);
@@ -338,6 +366,11 @@ int ma_test_muon_momentum(const ma_muon_group* group, float beta, int32_t nester
  * of the group is used. decay == 0 skips the decay term. */
 int ma_test_muon_update(const ma_muon_group* group, const void* u, int32_t u_dtype,
                         float c_lr, float c_wd, int32_t cautious, int32_t decay, void* stream);
+
+/* Makes the calling thread's next ma_muon_adamw_step fail with MA_ERR_HIP
+ * right after its fork (AdamW already queued on the side stream), as a launch
+ * failure there would: for testing that the join is still enqueued. */
+int ma_test_fail_after_fork(void);
 
 /* Newton-Schulz iteration alone: `count` dense m x n matrices (m <= n) in
  * x0 (DEVICE, dtype `precision`), result in u (DEVICE, same layout). */

@@ -221,6 +221,71 @@ def test_muon_adamw_step_validates_before_launch():
                                   s2) == L.MA_ERR_INVALID_ARG
 
 
+def test_muon_adamw_step_rejects_overlap_between_the_two_steps():
+    """AdamW runs concurrently with the Muon step, so an AdamW buffer over a
+    Muon buffer or the workspace is rejected before anything is enqueued."""
+    g, (p, gg, m) = group(rows=64, cols=128, count=2)
+    h, t = hp()
+    garr = (L.MuonGroupC * 1)(g)
+    lib = L.lib()
+    ws, nb = BASE * 4, 1 << 40
+    s1, s2 = C.c_void_p(0x1000), C.c_void_p(0x2000)
+    call = lambda sg: lib.ma_muon_adamw_step(garr, 1, C.byref(h), C.c_void_p(ws), nb,
+                                             (L.AdamWSegmentC * 1)(sg), 1, 256, s1, s2)
+    far = BASE * 2
+    ok = dict(param=far, grad=far + (1 << 24), exp_avg=far + (2 << 24), exp_avg_sq=far + (3 << 24))
+    # exp_avg over a Muon weight
+    assert call(seg(**{**ok, "exp_avg": p[1] + 128})) == L.MA_ERR_INVALID_ARG
+    assert "overlap" in lib.ma_last_error().decode()
+    # exp_avg_sq inside the workspace
+    assert call(seg(**{**ok, "exp_avg_sq": ws + 4096})) == L.MA_ERR_INVALID_ARG
+    # AdamW param over a Muon momentum buffer
+    assert call(seg(**{**ok, "param": m[0]})) == L.MA_ERR_INVALID_ARG
+
+
+def test_check_finite_field_and_query_validate():
+    g, k = group()
+    h, t = hp()
+    h.check_finite = 2
+    assert call_step(g, h) == L.MA_ERR_INVALID_ARG
+    lib = L.lib()
+    arr = (L.MuonGroupC * 1)(g)
+    flags = (C.c_int32 * 2)()
+    h0, t0 = hp()   # check_finite off: the step wrote no flags, so there is nothing to read
+    assert lib.ma_muon_nonfinite(arr, 1, C.byref(h0), C.c_void_p(BASE * 4), flags) == L.MA_ERR_INVALID_ARG
+    h1, t1 = hp(check_finite=True)
+    assert lib.ma_muon_nonfinite(arr, 1, C.byref(h1), None, flags) == L.MA_ERR_WORKSPACE
+    assert lib.ma_status_string(L.MA_ERR_NONFINITE) not in (b"ok", b"unknown status")
+    assert h1.check_finite == 1
+
+
+def test_missing_gradients_are_left_out_and_sparse_ones_rejected():
+    """The wrapper drops matrices and AdamW buffers whose gradient is None
+    (CPU tensors: only pointers are taken, nothing is launched)."""
+    import torch
+    from adamw_optimizer_step_amd import api
+    W = torch.zeros(3, 8, 16, dtype=torch.bfloat16)
+    Mo = torch.zeros_like(W)
+    G = [torch.zeros(8, 16, dtype=torch.bfloat16), None, torch.zeros(8, 16, dtype=torch.bfloat16)]
+    grp = api.MuonGroup(W, G, Mo)
+    assert grp.count == 2 and grp.kept == [0, 2]
+    step = 8 * 16 * 2
+    assert grp.p == [W.data_ptr(), W.data_ptr() + 2 * step] and grp.m == [Mo.data_ptr(), Mo.data_ptr() + 2 * step]
+    assert api.MuonGroup(W, None, Mo).count == 0
+    assert api.MuonGroup(W, torch.zeros_like(W), Mo).count == 3
+    sparse = torch.zeros(8, 16).to_sparse()
+    with pytest.raises(TypeError):
+        api.MuonGroup([W[0]], [sparse], [Mo[0]])
+    p = torch.zeros(10)
+    segs = [dict(param=p, grad=None, exp_avg=p, exp_avg_sq=p, lr=1.0, step=1),
+            dict(param=torch.zeros(4), grad=torch.zeros(4), exp_avg=torch.zeros(4), exp_avg_sq=torch.zeros(4),
+                 lr=1.0, step=1)]
+    arr, n = api._adamw_c(segs)
+    assert n == 1 and arr[0].n == 4
+    with pytest.raises(TypeError):
+        api._adamw_c([dict(param=p, grad=torch.zeros(10).to_sparse(), exp_avg=p, exp_avg_sq=p, lr=1.0, step=1)])
+
+
 def test_adamw_zero_segments_is_noop():
     assert L.lib().ma_adamw_step(None, 0, None) == L.MA_OK
     arr = (L.AdamWSegmentC * 1)(seg(n=0, param=None, grad=None, exp_avg=None, exp_avg_sq=None))

@@ -118,3 +118,43 @@ def test_overlapped_step_matches_sequential_step():
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
 
+
+
+@pytest.mark.parametrize("captured", [False, True])
+def test_failure_after_fork_still_joins(captured):
+    """A launch failing after the fork (forced by the library's test hook)
+    returns the error, but the caller's stream still waits for the AdamW work
+    already queued on the side stream: eagerly, AdamW is complete once the
+    caller's stream is synchronised; in a graph capture, the capture ends
+    normally (a side stream left unjoined would make it fail)."""
+    need_gpu()
+    import adamw_optimizer_step_amd as M
+    import oracle as O
+    from adamw_optimizer_step_amd import _lib as L
+    init_m, init_a = _state(9)
+    dm, da = _to_dev(init_m, init_a)
+    groups, hp, _ = _stepper(M, dm, da, None)
+    ws = torch.empty(max(1, M.muon_workspace_size(groups, hp)), dtype=torch.uint8, device=DEV)
+    _, _, step = _stepper(M, dm, da, ws, overlap=True)
+    say("failure after the fork", "captured" if captured else "eager")
+    if captured:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            L.check(L.lib().ma_test_fail_after_fork())
+            with pytest.raises(M.MuonAdamWError) as err:
+                step()
+        assert err.value.status == L.MA_ERR_HIP
+        torch.cuda.synchronize()
+        return
+    L.check(L.lib().ma_test_fail_after_fork())
+    with pytest.raises(M.MuonAdamWError) as err:
+        step()
+    assert err.value.status == L.MA_ERR_HIP and "injected" in str(err.value)
+    torch.cuda.current_stream(DEV).synchronize()
+    p, g, m, v = (t.numpy() for t in init_a)
+    ep, em, ev = O.adamw_step(p, g, m, v, 7, lr=float(np.float32(3e-4)), beta1=float(np.float32(0.9)),
+                              beta2=float(np.float32(0.95)), eps=float(np.float32(1e-8)),
+                              weight_decay=float(np.float32(0.1)))
+    for got, exp in ((da[0], ep), (da[2], em), (da[3], ev)):
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+    torch.cuda.synchronize()

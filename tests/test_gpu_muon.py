@@ -286,7 +286,10 @@ def test_step_is_deterministic():
         assert torch.equal(m0.view(torch.int16), m1.view(torch.int16))
 
 
-def _workload_check(name, seed=0, max_count=None, sample_per_group=None, ns_steps=None):
+def _workload_check(name, seed=0, max_count=None, sample_per_group=None, ns_steps=None, overlap=False):
+    """One step of a workload: Muon then AdamW on one stream, or (overlap) the
+    benchmark's launch, ma_muon_adamw_step with AdamW run by 256 lean
+    workgroups on a second stream beside the Newton-Schulz products."""
     import adamw_optimizer_step_amd as M
     wl = workload(name)
     data = materialize(wl, device=DEV, seed=seed, max_count=max_count)
@@ -295,8 +298,20 @@ def _workload_check(name, seed=0, max_count=None, sample_per_group=None, ns_step
              nesterov=wl.nesterov, ns_steps=ns_steps or wl.ns_steps, cautious=wl.cautious,
              equilibrate=wl.equilibrate, ns_precision=wl.ns_precision)
     mgs = [M.MuonGroup(d["W"], d["G"], d["M"]) for d in data["muon"]]
-    say("workload", name, [m.count for m in mgs])
-    ws = M.muon_step(mgs, hp)
+    segs = []
+    for a in data["adamw"]:
+        s = a["spec"]
+        segs.append(dict(param=a["p"], grad=a["g"], exp_avg=a["m"], exp_avg_sq=a["v"], step=a["step"],
+                         lr=f32r(s.lr), beta1=f32r(s.beta1), beta2=f32r(s.beta2), eps=f32r(s.eps),
+                         weight_decay=f32r(s.weight_decay)))
+    before = [(to_np(a["p"]), to_np(a["g"]), to_np(a["m"]), to_np(a["v"])) for a in data["adamw"]]
+    say("workload", name, [m.count for m in mgs], "overlapped" if overlap else "one stream")
+    if overlap and segs:
+        ws = M.optimizer_step(mgs, hp, segs, overlap=True, background_workgroups=256)
+    else:
+        ws = M.muon_step(mgs, hp)
+        if segs:
+            M.adamw_step(segs)
     torch.cuda.synchronize()
     dev = [(d["W"], d["G"], d["M"]) for d in data["muon"]]
     dts = (wl.param_dtype, wl.grad_dtype, wl.mom_dtype)
@@ -304,24 +319,13 @@ def _workload_check(name, seed=0, max_count=None, sample_per_group=None, ns_step
     if sample_per_group:
         sample = lambda n: sorted({0, n - 1, n // 2}) if sample_per_group >= 3 else sorted({0, n - 1})
     _check_step(host, dev, mgs, ws, hp, dts, sample=sample)
-    # AdamW segments of the workload: bit-exact
-    if data["adamw"]:
-        segs = []
-        for a in data["adamw"]:
-            s = a["spec"]
-            segs.append(dict(param=a["p"], grad=a["g"], exp_avg=a["m"], exp_avg_sq=a["v"], step=a["step"],
-                             lr=f32r(s.lr), beta1=f32r(s.beta1), beta2=f32r(s.beta2), eps=f32r(s.eps),
-                             weight_decay=f32r(s.weight_decay)))
-        before = [(to_np(a["p"]), to_np(a["g"]), to_np(a["m"]), to_np(a["v"])) for a in data["adamw"]]
-        say("workload adamw", name)
-        M.adamw_step(segs)
-        torch.cuda.synchronize()
-        for (p, g, m, v), s in zip(before, segs):
-            ep, em, ev = O.adamw_step(p, g, m, v, s["step"], lr=s["lr"], beta1=s["beta1"], beta2=s["beta2"],
-                                      eps=s["eps"], weight_decay=s["weight_decay"])
-            for got, exp in ((s["param"], ep), (s["exp_avg"], em), (s["exp_avg_sq"], ev)):
-                got = to_np(got)
-                assert bits_equal(got, exp), first_mismatch(got, exp)
+    # AdamW segments of the workload: bit-exact everywhere
+    for (p, g, m, v), s in zip(before, segs):
+        ep, em, ev = O.adamw_step(p, g, m, v, s["step"], lr=s["lr"], beta1=s["beta1"], beta2=s["beta2"],
+                                  eps=s["eps"], weight_decay=s["weight_decay"])
+        for got, exp in ((s["param"], ep), (s["exp_avg"], em), (s["exp_avg_sq"], ev)):
+            got = to_np(got)
+            assert bits_equal(got, exp), first_mismatch(got, exp)
 
 
 def test_workload_4L_d256_full():
@@ -329,10 +333,12 @@ def test_workload_4L_d256_full():
 
 
 def test_workload_12L_d1024_full_size_sampled():
-    """The 12-layer d=1024 set at full size, launched exactly as the benchmark
-    launches it; momentum and AdamW checked everywhere, updates and weights on
-    three matrices per group."""
-    _workload_check("c3_12L_d1024", sample_per_group=3)
+    """The 12-layer d=1024 set at full size, launched as the benchmark times
+    it: ma_muon_adamw_step, with AdamW on both 50304 x 1024 fp32 buffers by
+    256 lean workgroups on a second stream beside the Newton-Schulz products.
+    Momentum and AdamW are checked everywhere (bit-exact), updates and weights
+    on three matrices per group."""
+    _workload_check("c3_12L_d1024", sample_per_group=3, overlap=True)
 
 
 def test_workload_24L_d2048_reduced_count():
