@@ -25,6 +25,7 @@ MA_SCALE_NONE, MA_SCALE_SQRT_MAX1_R_OVER_C, MA_SCALE_MOONSHOT, MA_SCALE_SQRT_MAX
 MA_MAX_NS_STEPS = 16
 KERNEL_KINDS = ("rownorm", "finalize", "pre", "gram", "poly", "axpy", "post", "adamw", "lion")
 MA_WORKSPACE_ALIGN = 256
+MA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MuonGroupC(C.Structure):
@@ -67,6 +68,7 @@ EXPORTS = {
     "ma_muon_workspace_size": (C.c_size_t, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC)]),
     "ma_muon_step": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
                                C.c_size_t, C.c_void_p]),
+    "ma_muon_step_noalloc": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p]),
     "ma_muon_step_stats": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,
                                      C.c_size_t, C.c_void_p, C.c_void_p]),
     "ma_muon_nonfinite": (C.c_int, [C.POINTER(MuonGroupC), C.c_int32, C.POINTER(MuonHParamsC), C.c_void_p,

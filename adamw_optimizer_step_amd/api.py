@@ -201,6 +201,18 @@ def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[
     return workspace
 
 
+def muon_step_noalloc(groups: Sequence[MuonGroup], hp: MuonHParams, stream=None) -> None:
+    """``muon_step`` without a workspace (``ma_muon_step_noalloc``): the
+    library's fixed per-GPU scratch array stands in for it, so nothing is
+    allocated. For steps whose workspace fits in MA_NOALLOC_SCRATCH_BYTES;
+    calls that overlap on one GPU must be ordered by the caller."""
+    if not groups:
+        return
+    garr, keep = _groups_c(groups)
+    h, tab = hp.to_c()
+    L.check(L.lib().ma_muon_step_noalloc(garr, len(groups), C.byref(h), C.c_void_p(_stream(groups[0].device, stream))))
+
+
 def muon_nonfinite(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: torch.Tensor) -> List[bool]:
     """After a step with ``hp.check_finite`` (waits for the device): per matrix
     of ``groups`` (in order), whether its look-ahead momentum had non-finite

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <functional>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -561,8 +562,8 @@ struct FinalizeBatch {
 // Everything a Muon call checks before its first launch (no HIP call): the
 // plan, the workspace, and the byte range of every device buffer it touches,
 // appended to `rs` for the overlap check.
-// caller_ws false: the workspace is not the caller's (not checked, not in
-// `rs`).
+// caller_ws false: the workspace is the library's own scratch array
+// (ma_muon_step_noalloc; not checked, not in `rs`).
 int muon_prepare(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* workspace,
                  size_t workspace_bytes, float* stats, Plan& plan, std::vector<Range>& rs, bool caller_ws = true) {
   int rc = build_plan(groups, n_groups, hp, plan, true);
@@ -707,6 +708,53 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
 int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                  void* workspace, size_t workspace_bytes, void* stream) {
   return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// ma_muon_step_noalloc: the step's scratch memory in a fixed device array
+// ---------------------------------------------------------------------------
+// One copy per GPU the library runs on, held until the process ends. Host
+// code never uses `scratch` itself (its host-side name is not a device
+// address): the address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the device's first
+// call, with that device current).
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MA_ERR_INVALID_ARG, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+    if ((uintptr_t)ptr % MA_WORKSPACE_ALIGN) return fail(MA_ERR_WORKSPACE, "scratch array is not aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MA_OK;
+}
+}  // namespace
+
+int ma_muon_step_noalloc(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* stream) {
+  Plan plan;
+  std::vector<Range> rs;
+  int rc = muon_prepare(groups, n_groups, hp, nullptr, 0, nullptr, plan, rs, false);
+  if (rc) return rc;
+  if ((rc = check_overlaps(rs))) return rc;
+  if (plan.bytes > (size_t)MA_NOALLOC_SCRATCH_BYTES)
+    return fail(MA_ERR_WORKSPACE, "the step needs %zu bytes of scratch; ma_muon_step_noalloc has %zu (use ma_muon_step)",
+                plan.bytes, (size_t)MA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return muon_enqueue(plan, hp, ws, nullptr, stream);
 }
 
 int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,

@@ -172,6 +172,22 @@ size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
 int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ma_muon_step with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The step's scratch memory is a fixed
+ * array of MA_NOALLOC_SCRATCH_BYTES inside the library's device code, one
+ * per GPU, held until the process ends; the call allocates nothing. Same
+ * arguments, kernels and results as ma_muon_step. A call whose
+ * ma_muon_workspace_size exceeds MA_NOALLOC_SCRATCH_BYTES is rejected with
+ * MA_ERR_WORKSPACE before any launch. Every call on one GPU uses that GPU's
+ * one array: calls that may overlap on one GPU (on different streams, or
+ * from different host threads) race and must be ordered by the caller. Each
+ * call writes every byte of scratch it later reads, so nothing carries over
+ * from an earlier call. With check_finite, ma_muon_nonfinite is not available
+ * for this entry point (the flags live in the shared array). */
+#define MA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ma_muon_step_noalloc(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* stream);
+
 /* ma_muon_step that also reports, per matrix, the size of the step it took:
  * the per-layer ratio ||delta theta|| / ||theta|| that "3.9 Optimizers: SGD,
  * Adam, Adafactor, Lion, Muon & Shampoo" (section "Large-batch training:

@@ -243,6 +243,21 @@ def test_muon_adamw_step_rejects_overlap_between_the_two_steps():
     assert call(seg(**{**ok, "param": m[0]})) == L.MA_ERR_INVALID_ARG
 
 
+def test_noalloc_step_rejects_steps_beyond_its_scratch():
+    lib = L.lib()
+    h, t = hp()
+    small, k1 = group(rows=256, cols=1024, count=2)
+    need = lib.ma_muon_workspace_size((L.MuonGroupC * 1)(small), 1, C.byref(h))
+    assert 0 < need <= L.MA_NOALLOC_SCRATCH_BYTES
+    big, k2 = group(rows=1024, cols=4096, count=8)
+    assert lib.ma_muon_workspace_size((L.MuonGroupC * 1)(big), 1, C.byref(h)) > L.MA_NOALLOC_SCRATCH_BYTES
+    assert lib.ma_muon_step_noalloc((L.MuonGroupC * 1)(big), 1, C.byref(h), None) == L.MA_ERR_WORKSPACE
+    assert b"scratch" in lib.ma_last_error()
+    g, (p, gg, m) = group(rows=64, cols=128)
+    gg[0] = p[0] + 64          # the usual argument checks come first
+    assert lib.ma_muon_step_noalloc((L.MuonGroupC * 1)(g), 1, C.byref(h), None) == L.MA_ERR_INVALID_ARG
+
+
 def test_check_finite_field_and_query_validate():
     g, k = group()
     h, t = hp()
