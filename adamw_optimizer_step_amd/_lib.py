@@ -23,7 +23,7 @@ MA_BF16 = 1
 MA_EQ_OFF, MA_EQ_ROWS_PRE, MA_EQ_ROWS_POST, MA_EQ_ROWS_RMS = 0, 1, 2, 3
 MA_SCALE_NONE, MA_SCALE_SQRT_MAX1_R_OVER_C, MA_SCALE_MOONSHOT, MA_SCALE_SQRT_MAX = 0, 1, 2, 3
 MA_MAX_NS_STEPS = 16
-KERNEL_KINDS = ("rownorm", "finalize", "pre", "gram", "poly", "axpy", "post", "adamw", "lion")
+KERNEL_KINDS = ("rownorm", "finalize", "pre", "gram", "poly", "axpy", "post", "adamw", "lion", "axpy_update")
 MA_WORKSPACE_ALIGN = 256
 MA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -90,7 +90,7 @@ EXPORTS = {
     "ma_profile_begin": (C.c_int, [C.c_int32]),
     "ma_profile_end": (C.c_int, []),
     "ma_profile_read": (C.c_int, [C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
-    "ma_calib_mfma": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "ma_calib_mfma": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "ma_test_bf16_round": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
     "ma_test_muon_momentum": (C.c_int, [C.POINTER(MuonGroupC), C.c_float, C.c_int32, C.c_void_p,
                                         C.c_void_p]),

@@ -318,12 +318,15 @@ ElemArgs elem_args(const GroupPlan& p, const ma_muon_hparams* hp, unsigned char*
 // scaled (optional): per group, whether X0 holds Y with X0 = s Y, s in the
 // group's row-factor slot of row 0 of each matrix (k_finalize mode 4).
 // before_axpy (optional): called once, before the first AXPY launch is enqueued.
+// fused (optional): per group, the update to apply in the last AXPY's
+// epilogue (NsGroup::W null: none).
 // the AdamW fork of ma_muon_adamw_step: before product 3 * step + (GRAM 0,
 // POLY 1, AXPY 2) = the first AXPY
 constexpr int kForkAt = 2;
 int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int dtype,
                hipStream_t s, const std::vector<char>* scaled = nullptr,
-               const std::function<int()>* before_axpy = nullptr) {
+               const std::function<int()>* before_axpy = nullptr,
+               const std::vector<NsGroup>* fused = nullptr) {
   if (T == 0 || plan.g.empty()) return MA_OK;
   // groups with the most work per tile first (they set the tail of a launch)
   std::vector<int> order;
@@ -353,6 +356,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
         A.c = abc[3 * step + 2];
         const size_t nb = std::min(order.size() - base, (size_t)kMaxNsGroups);
         int rot = 0;
+        bool any_fused = false;
         for (size_t q = 0; q < nb; ++q) {
           const GroupPlan& p = plan.g[order[base + q]];
           NsGroup& G = A.g[q];
@@ -405,6 +409,20 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
           const bool sc = step == 0 && epi != EPI_POLY && scaled && (*scaled)[order[base + q]];
           G.scale = sc ? reinterpret_cast<const float*>(ws + p.off_rowf) : nullptr;
           G.scale_stride = p.row_stride;
+          if (epi == EPI_AXPY && last && fused && (*fused)[order[base + q]].W) {
+            const NsGroup& F = (*fused)[order[base + q]];
+            G.W = F.W;
+            G.sW = F.sW;
+            G.R = F.R;
+            G.C = F.C;
+            G.w_trans = F.w_trans;
+            G.cautious = F.cautious;
+            G.decay = F.decay;
+            G.c_lr = F.c_lr;
+            G.c_wd = F.c_wd;
+            G.nonfinite = F.nonfinite;
+            any_fused = true;
+          }
           G.unit = G.count >= 8 ? G.tiles : 1;
           G.rot = rot;
           rot = (rot + G.count * G.tiles / G.unit) & 7;
@@ -427,7 +445,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
         if (tile.dma) A.padded_blocks = 8 * std::min(per_xcd, kNsPersBlocksPerXcd);
         hipError_t err;
         {
-          ProfScope ps(MA_K_GRAM + epi, s);
+          ProfScope ps(any_fused ? MA_K_AXPY_UPDATE : MA_K_GRAM + epi, s);
           err = launch_ns_gemm(dtype, epi, tile, A, s);
         }
         if (err != hipSuccess) return hip_fail(err, "Newton-Schulz GEMM launch");
@@ -518,6 +536,32 @@ bool pre_rows_for(const GroupPlan& p, const ma_muon_hparams* hp) {
 }
 
 namespace {
+// Whether the iteration's result is row-scaled before the update (MuonEq
+// after the iteration, NorMuon): the update then waits for those factors.
+bool rows_after_ns(const ma_muon_hparams* hp) {
+  return hp->equilibrate == MA_EQ_ROWS_POST || hp->equilibrate == MA_EQ_ROWS_RMS;
+}
+
+// Whether the last AXPY can apply a group's update in its epilogue: a bf16
+// iteration with at least one step (the LDS-DMA kernel writes U), bf16
+// weights with rows of a multiple of 8 elements, stacked at one
+// 16-byte-aligned stride (*stride_elems), as same-shape matrices stored in one
+// tensor are.
+bool update_fusable(const GroupPlan& p, const ma_muon_hparams* hp, int64_t* stride_elems) {
+  if (p.count == 0 || !p.src || hp->ns_steps == 0 || p.dt_x != MA_BF16 || !ns_q_transposed(p.dt_x)) return false;
+  if (p.dt_p != MA_BF16) return false;
+  if (p.C % 8 != 0) return false;
+  const int64_t eb = dt_bytes(p.dt_p);
+  const uintptr_t w0 = (uintptr_t)p.src->params[0];
+  if (w0 % 16) return false;
+  const int64_t stride = p.count > 1 ? (int64_t)((uintptr_t)p.src->params[1] - w0) : p.R * p.C * eb;
+  if (stride < p.R * p.C * eb || stride % 16) return false;
+  for (int k = 2; k < p.count; ++k)
+    if ((uintptr_t)p.src->params[k] != w0 + (uintptr_t)(k * stride)) return false;
+  *stride_elems = stride / eb;
+  return true;
+}
+
 // k_finalize launches batched over groups: add() queues one group's
 // matrices, flush() launches what is queued (also when a batch fills).
 struct FinalizeBatch {
@@ -613,8 +657,8 @@ int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, f
   FinalizeBatch fin(hp, s);
   for (size_t gi = 0; gi < plan.g.size(); ++gi) {
     const GroupPlan& p = plan.g[gi];
-    if (p.count == 0) continue;
     scaled[gi] = pre_rows_for(p, hp) ? 1 : 0;
+    if (p.count == 0) continue;
     for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
       const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
       const ElemArgs a = elem_args(p, hp, ws, first, cnt);
@@ -648,12 +692,32 @@ int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, f
     }
   }
   // 4. T quintic steps
-  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s, &scaled, &fork_once);
+  // the update of groups whose weights the last AXPY can update in its
+  // epilogue (the separate update pass then skips them)
+  std::vector<NsGroup> fused(plan.g.size());
+  for (size_t gi = 0; gi < plan.g.size(); ++gi) {
+    const GroupPlan& p = plan.g[gi];
+    int64_t sw = 0;
+    if (!stats && !rows_after_ns(hp) && update_fusable(p, hp, &sw)) {
+      NsGroup& F = fused[gi];
+      F.W = p.src->params[0];
+      F.sW = sw;
+      F.R = (int32_t)p.R;
+      F.C = (int32_t)p.C;
+      F.w_trans = p.tall ? 1 : 0;
+      F.cautious = hp->cautious ? 1 : 0;
+      F.decay = hp->weight_decay != 0.0f ? 1 : 0;
+      F.c_lr = p.c_lr;
+      F.c_wd = p.c_wd;
+      F.nonfinite = hp->check_finite ? reinterpret_cast<const int32_t*>(ws + p.off_flags) : nullptr;
+    }
+  }
+  rc = enqueue_ns(plan, ws, hp->abc, hp->ns_steps, hp->ns_precision, s, &scaled, &fork_once, &fused);
   if (rc) return rc;
   // 5. (MuonEq POST, NorMuon: the update's row sums, one launch of the row
   // factors) and the update (and the update norms)
   const int ub = hp->ns_steps & 1;
-  const bool rows_after = hp->equilibrate == MA_EQ_ROWS_POST || hp->equilibrate == MA_EQ_ROWS_RMS;
+  const bool rows_after = rows_after_ns(hp);
   auto update_args = [&](const GroupPlan& p, int first, int cnt) {
     ElemArgs a = elem_args(p, hp, ws, first, cnt);
     a.xd = ws + p.off_direct(ub) + (size_t)(first * p.x_stride * dt_bytes(p.dt_x));
@@ -674,7 +738,9 @@ int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, f
     if ((rc = fin.flush())) return rc;
   }
   int64_t mat0 = 0;   // index of the group's first matrix in `stats`
-  for (const GroupPlan& p : plan.g) {
+  for (size_t gi = 0; gi < plan.g.size(); ++gi) {
+    const GroupPlan& p = plan.g[gi];
+    if (fused[gi].W) continue;   // updated by the last AXPY
     for (int first = 0; first < p.count; first += kMaxMatsPerLaunch) {
       const int cnt = std::min(kMaxMatsPerLaunch, p.count - first);
       ElemArgs a = update_args(p, first, cnt);
@@ -1052,10 +1118,10 @@ int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {
 // ---------------------------------------------------------------------------
 // calibration
 // ---------------------------------------------------------------------------
-int ma_calib_mfma(int32_t blocks, int32_t iters, float* sink, void* stream) {
-  if (blocks <= 0 || iters <= 0 || !sink || ((uintptr_t)sink & 3))
-    return fail(MA_ERR_INVALID_ARG, "blocks and iters must be > 0 and sink a 4-byte aligned pointer");
-  hipError_t err = launch_calib_mfma(blocks, iters, sink, reinterpret_cast<hipStream_t>(stream));
+int ma_calib_mfma(int32_t blocks, int32_t iters, int32_t changing, float* sink, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !sink || ((uintptr_t)sink & 3) || (changing != 0 && changing != 1))
+    return fail(MA_ERR_INVALID_ARG, "blocks and iters must be > 0, changing 0 or 1 and sink a 4-byte aligned pointer");
+  hipError_t err = launch_calib_mfma(blocks, iters, changing, sink, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? MA_OK : hip_fail(err, "calibration launch");
 }
 

@@ -4,6 +4,6 @@
 
 namespace ma {
 
-hipError_t launch_calib_mfma(int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_calib_mfma(int blocks, int iters, int changing, float* sink, hipStream_t s);
 
 }  // namespace ma

@@ -130,6 +130,23 @@ __device__ __forceinline__ void store1(void* p, int64_t i, float x) {
 template <int DT> constexpr int elem_bytes() { return DT == DT_BF16 ? 2 : 4; }
 
 // ----------------------------------------------------------------------------
+// The Muon update of one weight (cautious decoupled decay, then the step):
+//   mask = cautious ? (u*w >= 0) : true
+//   w1 = (decay && mask) ? w - c_wd*w : w;   return w1 - c_lr*u
+// one binary32 rounding per operation, no contraction (cautious weight decay
+// of the nanochat discussion "Stuck at the optimizer after figuring out
+// backward()", reply by mira687; decay and step both read the weight before
+// the update, "Chapter 4: The MuonAdamW Optimizer", section "The Full Muon
+// Step"). Shared by the update kernels and the fused update of the last
+// Newton-Schulz product, so that both give the same bits.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float muon_update(float w, float u, float c_lr, float c_wd, bool cautious, bool decay) {
+  const bool mask = cautious ? (__fmul_rn(u, w) >= 0.0f) : true;
+  const float w1 = (decay && mask) ? __fsub_rn(w, __fmul_rn(c_wd, w)) : w;
+  return __fsub_rn(w1, __fmul_rn(c_lr, u));
+}
+
+// ----------------------------------------------------------------------------
 // wavefront reduction (fixed order: butterfly over the 64 lanes)
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float x) {

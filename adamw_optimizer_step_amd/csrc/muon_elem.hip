@@ -403,10 +403,7 @@ __device__ __forceinline__ void block_sums_out(float sd, float sw, float* out) {
 }
 
 __device__ __forceinline__ float post_elem(float w, float u, float f, bool has_f, const ElemArgs& a) {
-  const float ue = has_f ? __fmul_rn(u, f) : u;
-  const bool mask = a.cautious ? (__fmul_rn(ue, w) >= 0.0f) : true;
-  const float w1 = (a.decay && mask) ? __fsub_rn(w, __fmul_rn(a.c_wd, w)) : w;
-  return __fsub_rn(w1, __fmul_rn(a.c_lr, ue));
+  return muon_update(w, has_f ? __fmul_rn(u, f) : u, a.c_lr, a.c_wd, a.cautious != 0, a.decay != 0);
 }
 
 constexpr int kPostChunks = 4;   // 8-element chunks per thread (vector path)

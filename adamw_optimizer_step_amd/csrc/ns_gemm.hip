@@ -145,6 +145,33 @@ __device__ __forceinline__ void stage4_strided(typename MfmaTraits<DT>::T* p, in
   }
 }
 
+// The fused update (see NsGroup::W; bf16 weights): the weight chunks a thread
+// updates are loaded before the tile's U is read back from LDS (wload), so
+// that their latency overlaps the staging barrier and the U stores; each
+// 8-value chunk at parameter row pr, columns pc .. pc+7 of matrix `mat` is
+// then updated with muon_update and written back (wapply). Both accesses
+// non-temporal.
+__device__ __forceinline__ bool w_in(const NsGroup& G, int pr, int pc) { return pr < G.R && pc < G.C; }
+__device__ __forceinline__ void wload(const NsGroup& G, int mat, int pr, int pc, uint4& w) {
+  if (!w_in(G, pr, pc)) return;   // padding of the iteration buffers
+  w = ld16<true>(reinterpret_cast<const uint16_t*>(G.W) + (int64_t)mat * G.sW + (int64_t)pr * G.C + pc);
+}
+__device__ __forceinline__ void wapply(const NsGroup& G, int mat, int pr, int pc, const uint4& wb, const uint4& ub) {
+  if (!w_in(G, pr, pc)) return;
+  const uint32_t uw[4] = {ub.x, ub.y, ub.z, ub.w}, ww[4] = {wb.x, wb.y, wb.z, wb.w};
+  float u[8], w[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u[2 * i] = __uint_as_float(uw[i] << 16);
+    u[2 * i + 1] = __uint_as_float(uw[i] & 0xFFFF0000u);
+    w[2 * i] = __uint_as_float(ww[i] << 16);
+    w[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = muon_update(w[e], u[e], G.c_lr, G.c_wd, G.cautious != 0, G.decay != 0);
+  store8<DT_BF16, true>(reinterpret_cast<uint16_t*>(G.W) + (int64_t)mat * G.sW + (int64_t)pr * G.C + pc, w);
+}
+
 template <int DT, int BM, int BN>
 struct EpiSmem {
   using Tr = MfmaTraits<DT>;
@@ -159,13 +186,15 @@ struct EpiSmem {
 // (l % 32) and columns 8q + 4(l/32) + 0..3; row-major staging then writes 8
 // bytes per lane, the transposed staging 2. The caller has finished with LDS
 // (a barrier precedes the call).
-template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false, bool ACC_T = false>
+template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false, bool ACC_T = false,
+          bool UPD = false>
 __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
                                             unsigned char* smem, int tid_in = -1) {
   using Tr = MfmaTraits<DT>;
   using T = typename Tr::T;
   using ES = EpiSmem<DT, BM, BN>;
+  static_assert(!UPD || (EPI == EPI_AXPY && DT == DT_BF16), "the update is fused into the bf16 AXPY only");
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -276,14 +305,28 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
           }
         }
       }
-    __syncthreads();
     T* dst = outT + (int64_t)mat * G.sT + (int64_t)(bj * BN) * G.ldT + bi * BM;
     constexpr int CPR = BM / VEC;   // 16-byte chunks per staged row
+    constexpr int NU = BN * CPR / NT;
+    const bool upd = UPD && G.W && G.w_trans && !(G.nonfinite && G.nonfinite[mat]);
+    uint4 wc[UPD ? NU : 1];
+    if constexpr (UPD) {
+      if (upd) {
 #pragma unroll
-    for (int u = 0; u < BN * CPR / NT; ++u) {
+        for (int u = 0; u < NU; ++u) {
+          const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
+          wload(G, mat, bj * BN + r, bi * BM + ch * VEC, wc[u]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
       const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldT + ch * VEC) =
-          *reinterpret_cast<const uint4*>(stg + r * ES::LDT + ch * VEC);
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * ES::LDT + ch * VEC);
+      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldT + ch * VEC) = v;
+      if constexpr (UPD)
+        if (upd) wapply(G, mat, bj * BN + r, bi * BM + ch * VEC, wc[u], v);
     }
     if (outN) __syncthreads();
   }
@@ -310,14 +353,28 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
           }
         }
       }
-    __syncthreads();
     T* dst = outN + (int64_t)mat * G.sN + (int64_t)(bi * BM) * G.ldN + bj * BN;
     constexpr int CPR = BN / VEC;
+    constexpr int NU = BM * CPR / NT;
+    const bool upd = UPD && G.W && !G.w_trans && !(G.nonfinite && G.nonfinite[mat]);
+    uint4 wc[UPD ? NU : 1];
+    if constexpr (UPD) {
+      if (upd) {
 #pragma unroll
-    for (int u = 0; u < BM * CPR / NT; ++u) {
+        for (int u = 0; u < NU; ++u) {
+          const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
+          wload(G, mat, bi * BM + r, bj * BN + ch * VEC, wc[u]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
       const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldN + ch * VEC) =
-          *reinterpret_cast<const uint4*>(stg + r * ES::LDN + ch * VEC);
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * ES::LDN + ch * VEC);
+      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldN + ch * VEC) = v;
+      if constexpr (UPD)
+        if (upd) wapply(G, mat, bi * BM + r, bj * BN + ch * VEC, wc[u], v);
     }
   }
 }
@@ -816,7 +873,7 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
 // is added inside the main loop by scaled-identity MFMAs against the Q
 // fragments, so the epilogue reads nothing back from global memory. AXPY
 // always folds.
-template <int EPI, bool FOLD, int WGM, int WGN, bool QT>
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD>
 __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem) {
   using namespace dma;
   using Gd = Grid<WGM, WGN>;
@@ -948,7 +1005,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true>(args, G, J, acc, smem, tid);
+  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true, UPD>(args, G, J, acc, smem, tid);
 }
 
 // Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
@@ -957,7 +1014,9 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
 // the longest jobs first and, where jobs differ in K, a fixed stride ends
 // about as late as taking jobs on demand would (the blocks holding one long
 // and two short jobs set the end either way).
-template <int EPI, bool FOLD, int WGM, int WGN, bool QT>
+// UPD: the AXPY of the last step, which also applies the Muon update to the
+// weights of the groups that carry one (NsGroup::W)
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD>
 __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 ns_gemm_dma(const NsArgs args) {
   using namespace dma;
@@ -969,7 +1028,7 @@ ns_gemm_dma(const NsArgs args) {
   const int P = (int)(gridDim.x >> 3);
   TileJob J;
   for (int local = (int)(blockIdx.x >> 3); map_job_at(args, x, local, J); local += P) {
-    dma_tile<EPI, FOLD, WGM, WGN, QT>(args, J, smem);
+    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD>(args, J, smem);
     __syncthreads();   // the epilogue is done with LDS before the next job's DMA
   }
 }
@@ -994,9 +1053,9 @@ static hipError_t launch_reg_epi(int epi, const NsArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int EPI, bool FOLD, int WGM, int WGN, bool QT = false>
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT = false, bool UPD = false>
 static hipError_t launch_dma(const NsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD, WGM, WGN, QT>), dim3(a.padded_blocks), dim3(64 * WGM * WGN), 0, s, a);
+  hipLaunchKernelGGL((ns_gemm_dma<EPI, FOLD, WGM, WGN, QT, UPD>), dim3(a.padded_blocks), dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1005,7 +1064,12 @@ static hipError_t launch_dma_epi(int epi, bool qt, const NsArgs& a, hipStream_t 
   if (qt) {
     // AXPY with Q read transposed (8-wave form only)
     if constexpr (WGM == 2 && WGN == 4) {
-      if (epi == EPI_AXPY) return launch_dma<EPI_AXPY, true, WGM, WGN, true>(a, s);
+      if (epi == EPI_AXPY) {
+        bool upd = false;
+        for (int q = 0; q < a.n_groups; ++q) upd = upd || a.g[q].W != nullptr;
+        return upd ? launch_dma<EPI_AXPY, true, WGM, WGN, true, true>(a, s)
+                   : launch_dma<EPI_AXPY, true, WGM, WGN, true, false>(a, s);
+      }
     }
     return hipErrorInvalidValue;
   }

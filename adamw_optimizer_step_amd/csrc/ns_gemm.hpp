@@ -41,6 +41,17 @@ struct NsGroup {
   // X' of s X given B of s X)
   const float* scale;
   int64_t scale_stride;
+  // Fused update (AXPY of the last step, bf16 iteration; W null: none). Matrix
+  // k's weight, bf16, row-major R x C with C % 8 == 0, at W + k * sW elements
+  // (16-byte aligned), takes the Muon update with
+  // the stored U tile in the parameter's layout: rows i of outN, or rows j of
+  // outT for a tall matrix (w_trans); matrices with nonfinite[k] != 0 are
+  // left unchanged.
+  void* W;
+  int64_t sW;
+  int32_t R, C, w_trans, cautious, decay;
+  float c_lr, c_wd;
+  const int32_t* nonfinite;
 };
 
 // Scheduling: the hardware deals consecutive workgroups round-robin to the 8

@@ -345,7 +345,8 @@ typedef enum {
   MA_K_POST = 6,      /* cautious decay and the update */
   MA_K_ADAMW = 7,
   MA_K_LION = 8,
-  MA_K_COUNT = 9
+  MA_K_AXPY_UPDATE = 9, /* the last AXPY of a step with the update fused into it */
+  MA_K_COUNT = 10
 } ma_kernel_kind;
 
 int ma_profile_begin(int32_t max_launches);
@@ -358,9 +359,12 @@ int ma_profile_read(int32_t kind, double* total_ms, int64_t* launches);
  * GEMMs are compared with. Launches `blocks` workgroups of 4 waves; each
  * wave issues iters x 16 independent 32x32x16 bf16 MFMAs (32768 flops each)
  * on register operands and stores one float per lane into sink (DEVICE,
- * blocks x 256 floats, 4-byte aligned). Time it with events on `stream`.
+ * blocks x 256 floats, 4-byte aligned). changing = 0: near-constant
+ * operands; 1: random operands that change from one MFMA to the next, as a
+ * real product's do (more switching, more power, and under the part's power
+ * limit a lower clock). Time it with events on `stream`.
  * ------------------------------------------------------------------------- */
-int ma_calib_mfma(int32_t blocks, int32_t iters, float* sink, void* stream);
+int ma_calib_mfma(int32_t blocks, int32_t iters, int32_t changing, float* sink, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Stage entry points, used by the test suite to check single stages with

@@ -357,7 +357,8 @@ def test_hparams_table():
 
 def test_calib_mfma_validates():
     lib = L.lib()
-    assert lib.ma_calib_mfma(0, 10, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
-    assert lib.ma_calib_mfma(4, 0, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
-    assert lib.ma_calib_mfma(4, 10, None, None) == L.MA_ERR_INVALID_ARG
-    assert lib.ma_calib_mfma(4, 10, C.c_void_p(BASE + 2), None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(0, 10, 0, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 0, 0, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 10, 0, None, None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 10, 2, C.c_void_p(BASE), None) == L.MA_ERR_INVALID_ARG
+    assert lib.ma_calib_mfma(4, 10, 0, C.c_void_p(BASE + 2), None) == L.MA_ERR_INVALID_ARG

@@ -9,7 +9,12 @@
   kernels normalise in fp32, the oracle in float64) and to the bf16
   iteration's bound with five steps.
 Shapes cover the vector path (rows a multiple of 8) and the tile path (odd
-columns), bf16 and fp32 weights.
+columns), bf16 and fp32 weights, wide, square and tall matrices.
+
+A step with stats applies the update in its own pass; a plain step applies it
+in the epilogue of the last Newton-Schulz product wherever the weights allow
+(bf16, rows a multiple of 8 elements, one stride between matrices): the
+weights both write must be the same bits.
 """
 import numpy as np
 import pytest
@@ -22,7 +27,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
-SHAPES = [((256, 256), 3, "bf16"), ((37, 53), 2, "bf16"), ((300, 100), 2, "f32"), ((128, 512), 2, "f32")]
+SHAPES = [((256, 256), 3, "bf16"), ((37, 53), 2, "bf16"), ((300, 100), 2, "f32"), ((128, 512), 2, "f32"),
+          ((520, 264), 2, "bf16"), ((136, 392), 3, "bf16")]
 
 
 def _groups(seed):
