@@ -19,11 +19,12 @@ size is checked through properties that hold at any size:
 Tolerance of the closed-form check: the stored bf16 gradient carries a
 relative rounding of about 2^-9, which the iteration amplifies in the small
 singular directions, and every bf16 rounding point inside the iteration adds
-to it. The bf16-emulating oracle itself lands 0.04 to 0.05 from the closed
-form on these matrices (tests/golden/closed_form_bf16_error.json, written by
-the script beside it from the oracle alone); the GPU result may be at most
-1.25 times the oracle's distance for the same matrix. The 64 largest
-directions are checked to the bf16 bar of 2e-2.
+to it. The bf16-emulating oracle itself lands 0.002 (one step) to 0.044
+(five steps) from the closed form on these matrices
+(tests/golden/closed_form_bf16_error.json, written by the script beside it
+from the oracle alone); the GPU result may be at most 1.02 times the
+oracle's distance for the same matrix. The 64 largest directions are checked
+to the bf16 bar of 2e-2.
 """
 import json
 import math
@@ -43,8 +44,11 @@ DEV = torch.device("cuda:0")
 KJ = (3.4445, -4.7750, 2.0315)
 
 
-# the GPU's distance to the closed form may exceed the bf16 oracle's own by this factor
-RATIO = 1.25
+# the GPU's distance to the closed form may exceed the bf16 oracle's own by this
+# factor: measured on MI355X, the two agree to 3-4 significant digits at
+# ns_steps 1, 3 and 5 (the largest GPU/oracle ratio over the 18 matrices was
+# 1.0015), so 2% is the slack kept for rounding differences
+RATIO = 1.02
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_form_bf16_error.json")
 
 
