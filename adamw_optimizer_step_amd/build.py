@@ -29,6 +29,10 @@ FLAGS = [
 ]
 
 
+# roctx, for the library's host-side ranges (rocprofv3 --marker-trace)
+LINK = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
@@ -73,7 +77,7 @@ def build_host_sanitized(verbose: bool = True) -> str:
             fresh = os.path.exists(obj) and os.path.getmtime(obj) >= max(
                 os.path.getmtime(f) for f in glob.glob(os.path.join(CSRC, "*")))
             objs.append(obj if fresh else _compile(src))
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", SAN_LIB],
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", SAN_LIB],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
@@ -95,7 +99,7 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -13,6 +13,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/muon_adamw.h"
 #include "adamw.hpp"
 #include "lion.hpp"
@@ -63,6 +65,32 @@ struct ProfScope {
   ~ProfScope() {
     if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
   }
+};
+
+// ----------------------------------------------------------------------------
+// roctx ranges on the calling thread (rocprofv3 --marker-trace): every entry
+// point that enqueues work is one range, and the Muon step's phases nest in
+// it. They span the host's enqueueing, not the GPU's execution.
+// ----------------------------------------------------------------------------
+struct EntryMark {
+  explicit EntryMark(const char* what) { roctxRangePushA(what); }
+  ~EntryMark() { roctxRangePop(); }
+  EntryMark(const EntryMark&) = delete;
+  EntryMark& operator=(const EntryMark&) = delete;
+};
+
+struct PhaseMark {
+  bool open = false;
+  void enter(const char* what) {
+    leave();
+    roctxRangePushA(what);
+    open = true;
+  }
+  void leave() {
+    if (open) roctxRangePop();
+    open = false;
+  }
+  ~PhaseMark() { leave(); }
 };
 
 inline int64_t dt_bytes(int dt) { return dt == MA_BF16 ? 2 : 4; }
@@ -650,9 +678,11 @@ int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, f
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   hipError_t err;
+  PhaseMark phase;
   // 1. per group: the row pass (momentum, row sums and the row-scaled X0), or
   // the row sums alone; 2. one launch of the per-matrix factors for every
   // group; 3. per two-pass group: the momentum update and X0
+  phase.enter("muon: momentum, norms, X0");
   std::vector<char> scaled(plan.g.size(), 0);
   FinalizeBatch fin(hp, s);
   for (size_t gi = 0; gi < plan.g.size(); ++gi) {
@@ -692,6 +722,7 @@ int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, f
     }
   }
   // 4. T quintic steps
+  phase.enter("muon: Newton-Schulz");
   // the update of groups whose weights the last AXPY can update in its
   // epilogue (the separate update pass then skips them)
   std::vector<NsGroup> fused(plan.g.size());
@@ -716,6 +747,7 @@ int muon_enqueue(const Plan& plan, const ma_muon_hparams* hp, void* workspace, f
   if (rc) return rc;
   // 5. (MuonEq POST, NorMuon: the update's row sums, one launch of the row
   // factors) and the update (and the update norms)
+  phase.enter("muon: update");
   const int ub = hp->ns_steps & 1;
   const bool rows_after = rows_after_ns(hp);
   auto update_args = [&](const GroupPlan& p, int first, int cnt) {
@@ -773,6 +805,7 @@ int muon_step_impl(const ma_muon_group* groups, int32_t n_groups, const ma_muon_
 
 int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                  void* workspace, size_t workspace_bytes, void* stream) {
+  EntryMark mark("ma_muon_step");
   return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, nullptr, stream);
 }
 
@@ -810,6 +843,7 @@ int scratch_for_current_device(void** out) {
 }  // namespace
 
 int ma_muon_step_noalloc(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* stream) {
+  EntryMark mark("ma_muon_step_noalloc");
   Plan plan;
   std::vector<Range> rs;
   int rc = muon_prepare(groups, n_groups, hp, nullptr, 0, nullptr, plan, rs, false);
@@ -825,6 +859,7 @@ int ma_muon_step_noalloc(const ma_muon_group* groups, int32_t n_groups, const ma
 
 int ma_muon_step_stats(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                        void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  EntryMark mark("ma_muon_step_stats");
   if (!stats || ((uintptr_t)stats & 3)) return fail(MA_ERR_INVALID_ARG, "stats is null or not 4-byte aligned");
   return muon_step_impl(groups, n_groups, hp, workspace, workspace_bytes, stats, stream);
 }
@@ -998,6 +1033,7 @@ thread_local bool g_fail_after_fork = false;
 int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                        void* workspace, size_t workspace_bytes, const ma_adamw_segment* segs, int32_t n_segs,
                        int32_t workgroups, void* stream, void* side_stream) {
+  EntryMark mark("ma_muon_adamw_step");
   if (workgroups < 1) return fail(MA_ERR_INVALID_ARG, "workgroups must be >= 1");
   if (side_stream == stream) return fail(MA_ERR_INVALID_ARG, "side_stream must differ from stream");
   // every argument of both steps, and one overlap check over the buffers of
@@ -1021,6 +1057,7 @@ int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_m
     if ((err = hipEventRecord(e_fork, s)) != hipSuccess) return hip_fail(err, "fork record");
     if ((err = hipStreamWaitEvent(side, e_fork, 0)) != hipSuccess) return hip_fail(err, "fork wait");
     side_waits = true;
+    EntryMark side_mark("adamw on the side stream");
     const int r = adamw_enqueue(segs, n_segs, workgroups, side_stream);
     if (r == MA_OK && inject) return fail(MA_ERR_HIP, "failure injected after the fork (test hook)");
     return r;
@@ -1043,15 +1080,18 @@ int ma_test_fail_after_fork(void) {
 }
 
 int ma_adamw_step(const ma_adamw_segment* segs, int32_t n, void* stream) {
+  EntryMark mark("ma_adamw_step");
   return adamw_impl(segs, n, 0, stream);
 }
 
 int ma_adamw_step_background(const ma_adamw_segment* segs, int32_t n, int32_t workgroups, void* stream) {
+  EntryMark mark("ma_adamw_step_background");
   if (workgroups < 1) return fail(MA_ERR_INVALID_ARG, "workgroups must be >= 1");
   return adamw_impl(segs, n, workgroups, stream);
 }
 
 int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {
+  EntryMark mark("ma_lion_step");
   if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
   std::vector<Range> rs;
   for (int i = 0; i < n; ++i) {

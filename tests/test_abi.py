@@ -32,6 +32,14 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(h, name), name
 
 
+def test_library_links_roctx():
+    """The entry points mark their host-side work as roctx ranges, so the
+    library needs the roctx runtime (a no-op unless a profiler is attached)."""
+    import subprocess
+    out = subprocess.run(["readelf", "-d", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert re.search(r"NEEDED.*librocprofiler-sdk-roctx", out), out
+
+
 def test_status_strings_and_version():
     lib = L.lib()
     assert lib.ma_status_string(0) == b"ok"
