@@ -126,6 +126,14 @@ NsTile ns_tile(int dtype, bool /*symmetric*/) {
   return {256, 256, ns_dma_bk(), 2, 4, 1};
 }
 
+// An fp32 launch with fewer 128 x 128 jobs than this takes 64 x 64 tiles (2 x 2
+// waves of 32 x 32): a few long jobs would leave most of the 256 CUs idle, and
+// a quarter of the tile runs its K loop in a quarter of the time. Both tiles
+// accumulate every output over k in the same order with the same
+// instructions, so they give the same bits.
+constexpr int kF32SmallLaunchJobs = 128;
+constexpr NsTile kF32SmallTile = {64, 64, 32, 2, 2, 0};
+
 // ----------------------------------------------------------------------------
 // plan of one Muon call
 // ----------------------------------------------------------------------------
@@ -371,18 +379,28 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
         const int rc = (*before_axpy)();
         if (rc) return rc;
       }
-      NsTile tile = ns_tile(dtype, epi != EPI_AXPY);
+      NsTile tile0 = ns_tile(dtype, epi != EPI_AXPY);
       const bool qt = epi == EPI_AXPY && ns_q_transposed(dtype);
-      tile.qt = qt ? 1 : 0;
+      tile0.qt = qt ? 1 : 0;
       // B is stored as its upper triangle when AXPY reads the rest transposed
       const bool b_upper = ns_b_upper(dtype);
-      if (epi != EPI_AXPY && tile.bm != tile.bn) return fail(MA_ERR_INVALID_ARG, "symmetric GEMM tile must be square");
+      if (epi != EPI_AXPY && tile0.bm != tile0.bn) return fail(MA_ERR_INVALID_ARG, "symmetric GEMM tile must be square");
       for (size_t base = 0; base < order.size(); base += kMaxNsGroups) {
+        const size_t nb = std::min(order.size() - base, (size_t)kMaxNsGroups);
+        NsTile tile = tile0;
+        if (!tile.dma) {
+          int64_t jobs = 0;
+          for (size_t q = 0; q < nb; ++q) {
+            const GroupPlan& p = plan.g[order[base + q]];
+            const int64_t tm = p.m_pad / tile.bm, tn = p.n_pad / tile.bn;
+            jobs += p.count * (epi == EPI_AXPY ? tm * tn : tm * (tm + 1) / 2);
+          }
+          if (jobs < kF32SmallLaunchJobs) tile = kF32SmallTile;
+        }
         NsArgs A{};
         A.a = abc[3 * step];
         A.b = abc[3 * step + 1];
         A.c = abc[3 * step + 2];
-        const size_t nb = std::min(order.size() - base, (size_t)kMaxNsGroups);
         int rot = 0;
         bool any_fused = false;
         for (size_t q = 0; q < nb; ++q) {

@@ -25,7 +25,8 @@
 //    Blocks are persistent, one per CU, each walking a fixed share of its
 //    XCD's tile list.
 //  * ns_gemm_reg (fp32): a register-staged double-buffered kernel,
-//    128 x 128 x 32 tiles of 2 x 2 waves on 32x32x2 fp32 MFMAs.
+//    128 x 128 x 32 tiles of 2 x 2 waves on 32x32x2 fp32 MFMAs (64 x 64 x 32
+//    for launches with few jobs).
 // Blocks are dealt to the 8 XCDs so that each XCD gets an eighth of every
 // shape group, whole matrices at a time where possible (see NsArgs).
 #include "ns_gemm.hpp"
@@ -1098,6 +1099,7 @@ hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipS
   } else {
     constexpr int DTv = DT_F32;
     MA_REG_TILE(128, 128, 32, 2, 2)
+    MA_REG_TILE(64, 64, 32, 2, 2)   // launches with few jobs
   }
   return hipErrorInvalidValue;
 }

@@ -55,6 +55,24 @@ def test_newton_schulz_matches_oracle(prec, m, n, count, steps):
         assert err <= TOL[prec], (k, err)
 
 
+def test_f32_tile_sizes_give_the_same_bits():
+    """An fp32 launch with few jobs runs 64 x 64 tiles, a larger one 128 x 128.
+    Both accumulate each output over k in the same order with the same MFMAs,
+    so a matrix iterated alone (3 Gram jobs at 128 x 128: the small tiles)
+    gives the bits it gets among 47 others (144 Gram jobs, 768 AXPY jobs: the
+    large tiles); the large-tile launch also meets the fp32 bar."""
+    import adamw_optimizer_step_amd as M
+    x0 = _x0(48, 256, 1024, 77, torch.float32)
+    say("ns f32 tiles: 48 matrices of 256x1024")
+    many = to_np(M.newton_schulz(x0.to(DEV), KJ, 5))
+    for k in (0, 47):
+        say("ns f32 tiles: matrix", k, "alone")
+        alone = to_np(M.newton_schulz(x0[k:k + 1].to(DEV), KJ, 5))[0]
+        assert bits_equal(alone, many[k]), first_mismatch(alone, many[k])
+    ref = O.newton_schulz(to_np(x0[47]).astype(np.float64), KJ, "f64", 5)
+    assert rel_fro(many[47], ref) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 def test_newton_schulz_special_coefficients(prec):
     """(1,0,0) copies X exactly; (0,1,0) gives X X^T X; (0,0,1) gives (X X^T)^2 X."""
