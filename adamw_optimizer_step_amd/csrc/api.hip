@@ -134,6 +134,27 @@ NsTile ns_tile(int dtype, bool /*symmetric*/) {
 constexpr int kF32SmallLaunchJobs = 128;
 constexpr NsTile kF32SmallTile = {64, 64, 32, 2, 2, 0};
 
+// Such a launch's Gram product (K = the long side, up to 4x the short one)
+// is also split along K into up to 4 slices of whole 256-column blocks, so
+// that its jobs x slices stay within this many blocks: each slice's partial
+// product goes to a workspace buffer of its own, and k_split_sum adds the
+// slices in order (deterministic, but rounded differently from one pass over
+// K) and applies the deferred Frobenius factor.
+constexpr int kF32SplitMaxBlocks = 256;
+
+// Slices for an fp32 group's Gram product when launched alone: 1 (no split)
+// unless the group takes the 64 x 64 tiles and K spans at least two
+// 256-column blocks; the slice count divides those blocks.
+int f32_gram_split(int64_t count, int64_t m_pad, int64_t n_pad) {
+  const int64_t t128 = m_pad / 128, t64 = m_pad / 64;
+  if (count * t128 * (t128 + 1) / 2 >= kF32SmallLaunchJobs) return 1;
+  const int64_t jobs = count * t64 * (t64 + 1) / 2;
+  const int64_t kb = n_pad / 256;
+  int sl = (int)std::min<int64_t>({4, kb, kF32SplitMaxBlocks / std::max<int64_t>(jobs, 1)});
+  while (sl > 1 && kb % sl) --sl;
+  return sl;
+}
+
 // ----------------------------------------------------------------------------
 // plan of one Muon call
 // ----------------------------------------------------------------------------
@@ -147,6 +168,8 @@ struct GroupPlan {
   size_t off_x[2], off_xt[2], off_a, off_b, off_rowsq, off_rowf;   // bytes
   size_t off_part;           // update-norm partial sums: count x ppm_max x 2 floats
   size_t off_flags;          // non-finite flags: count int32
+  int gram_split;            // fp32 Gram product split along K into this many slices (1: none)
+  size_t off_gpart;          // their partial products: gram_split x count x a_stride floats
   bool check_finite;
   int ppm_max;
   const ma_muon_group* src;
@@ -194,6 +217,9 @@ void plan_group(GroupPlan& p, int64_t R, int64_t C, int count, int dt_x, size_t&
   p.ppm_max = post_blocks_per_mat_max(R, C);
   p.off_part = off;  off = align_up(off + (size_t)count * p.ppm_max * 2 * 4, MA_WORKSPACE_ALIGN);
   p.off_flags = off; off = align_up(off + (size_t)count * 4, MA_WORKSPACE_ALIGN);
+  p.gram_split = dt_x == MA_F32 ? f32_gram_split(count, p.m_pad, p.n_pad) : 1;
+  p.off_gpart = off;
+  if (p.gram_split > 1) off = align_up(off + (size_t)p.gram_split * count * p.a_stride * 4, MA_WORKSPACE_ALIGN);
 }
 
 int validate_hparams(const ma_muon_hparams* hp) {
@@ -475,10 +501,46 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
         }
         (void)e;
         A.n_groups = (int32_t)nb;
+        // an fp32 Gram launch of few long jobs: every group's K in `split`
+        // slices, each slice a group of its own writing a partial product
+        int split = 1;
+        if (epi == EPI_GRAM && !tile.dma && tile.bm == kF32SmallTile.bm) {
+          split = 4;
+          int64_t jobs = 0;
+          for (size_t q = 0; q < nb; ++q) {
+            split = std::min(split, plan.g[order[base + q]].gram_split);
+            jobs += (int64_t)A.g[q].count * A.g[q].tiles;
+          }
+          if (split < 2 || (int)nb * split > kMaxNsGroups || jobs * split > kF32SplitMaxBlocks) split = 1;
+          for (size_t q = 0; q < nb && split > 1; ++q)
+            if ((A.g[q].K / 256) % split) split = 1;
+        }
+        if (split > 1) {
+          NsArgs S = A;
+          int k = 0;
+          rot = 0;
+          for (size_t q = 0; q < nb; ++q) {
+            const GroupPlan& p = plan.g[order[base + q]];
+            const int32_t kc = A.g[q].K / split;
+            for (int sl = 0; sl < split; ++sl, ++k) {
+              NsGroup G = A.g[q];
+              G.P = G.Q = reinterpret_cast<const unsigned char*>(A.g[q].P) + (size_t)sl * kc * e;
+              G.K = kc;
+              void* part = ws + p.off_gpart + (size_t)sl * p.count * p.a_stride * e;
+              G.outN = G.outT = part;
+              G.scale = nullptr;   // applied to the sum
+              G.rot = rot;
+              rot = (rot + G.count * G.tiles / G.unit) & 7;
+              S.g[k] = G;
+            }
+          }
+          S.n_groups = k;
+          A = S;
+        }
         int per_xcd = 0;
         for (int x = 0; x < 8; ++x) {
           int jx = 0;
-          for (size_t q = 0; q < nb; ++q) {
+          for (int q = 0; q < A.n_groups; ++q) {
             const NsGroup& G = A.g[q];
             const int units = G.count * G.tiles / G.unit;
             const int u0 = (x - G.rot + 8) & 7;
@@ -495,6 +557,31 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
           err = launch_ns_gemm(dtype, epi, tile, A, s);
         }
         if (err != hipSuccess) return hip_fail(err, "Newton-Schulz GEMM launch");
+        if (split > 1) {
+          SplitSumArgs R{};
+          R.n = (int32_t)nb;
+          int64_t blocks = 0;
+          for (size_t q = 0; q < nb; ++q) {
+            const GroupPlan& p = plan.g[order[base + q]];
+            SplitSumGroup& g = R.g[q];
+            g.part = reinterpret_cast<const float*>(ws + p.off_gpart);
+            g.out = reinterpret_cast<float*>(ws + p.off_a);
+            g.split_stride = (int64_t)p.count * p.a_stride;
+            g.mat_elems = p.a_stride;
+            g.slices = split;
+            const bool sc = step == 0 && scaled && (*scaled)[order[base + q]];
+            g.scale = sc ? reinterpret_cast<const float*>(ws + p.off_rowf) : nullptr;
+            g.scale_stride = p.row_stride;
+            g.block_begin = blocks;
+            blocks += g.split_stride / kSplitSumBlockElems;
+          }
+          R.blocks = blocks;
+          {
+            ProfScope ps(MA_K_GRAM, s);
+            err = launch_split_sum(R, s);
+          }
+          if (err != hipSuccess) return hip_fail(err, "Gram slice sum");
+        }
       }
     }
   }

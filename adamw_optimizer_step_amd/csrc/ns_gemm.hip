@@ -1089,6 +1089,45 @@ static hipError_t launch_dma_epi(int epi, bool qt, const NsArgs& a, hipStream_t 
 
 int ns_dma_bk() { return dma::BK; }
 
+// ---------------------------------------------------------------------------
+// sum of the K slices of a split fp32 Gram product (see SplitSumArgs)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_split_sum(const SplitSumArgs a) {
+  const int64_t b = blockIdx.x;
+  int q = 0;
+#pragma unroll 1
+  while (q + 1 < a.n && b >= a.g[q + 1].block_begin) ++q;
+  const SplitSumGroup& g = a.g[q];
+  const int64_t i = (b - g.block_begin) * kSplitSumBlockElems + (int64_t)threadIdx.x * 4;
+  float4 v = *reinterpret_cast<const float4*>(g.part + i);
+#pragma unroll 1
+  for (int sl = 1; sl < g.slices; ++sl) {
+    const float4 w = *reinterpret_cast<const float4*>(g.part + sl * g.split_stride + i);
+    v.x = __fadd_rn(v.x, w.x);
+    v.y = __fadd_rn(v.y, w.y);
+    v.z = __fadd_rn(v.z, w.z);
+    v.w = __fadd_rn(v.w, w.w);
+  }
+  if (g.scale) {
+    // the Gram product of X = s Y is s^2 Y Y^T, as in the unsplit epilogue
+    float sc = g.scale[(i / g.mat_elems) * g.scale_stride];
+    sc = sc * sc;
+    v.x *= sc;
+    v.y *= sc;
+    v.z *= sc;
+    v.w *= sc;
+  }
+  *reinterpret_cast<float4*>(g.out + i) = v;
+}
+
+hipError_t launch_split_sum(const SplitSumArgs& a, hipStream_t s) {
+  if (a.blocks <= 0) return hipSuccess;
+  for (int q = 0; q < a.n; ++q)
+    if (a.g[q].mat_elems % kSplitSumBlockElems || a.g[q].slices < 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_split_sum, dim3((unsigned)a.blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipStream_t s) {
   if (a.padded_blocks <= 0) return hipSuccess;
   if (dtype == DT_BF16) {

@@ -83,6 +83,29 @@ struct NsTile { int bm, bn, bk, wgm, wgn, dma, qt = 0; };
 
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& args, hipStream_t s);
 
+// Sum of the K slices of a split fp32 Gram product (k_split_sum): per group,
+// out[i] = (part_0[i] + part_1[i] + ...) in slice order, times the matrix's
+// deferred Frobenius factor squared when `scale` is set, over count matrices
+// of mat_elems floats (a multiple of kSplitSumBlockElems). Blocks
+// block_begin .. of the launch belong to the group.
+constexpr int kSplitSumBlockElems = 1024;   // 256 threads x 4 floats
+struct SplitSumGroup {
+  const float* part;
+  float* out;
+  const float* scale;
+  int64_t scale_stride;     // floats between matrices' factors
+  int64_t mat_elems;        // floats per matrix
+  int64_t split_stride;     // floats between slices (count x mat_elems)
+  int64_t block_begin;
+  int32_t slices;
+};
+struct SplitSumArgs {
+  int32_t n;
+  int64_t blocks;
+  SplitSumGroup g[kMaxNsGroups];
+};
+hipError_t launch_split_sum(const SplitSumArgs& args, hipStream_t s);
+
 // k-tile of the LDS-DMA kernel (its block tile is 256 x 256, 2 x 2 waves)
 int ns_dma_bk();
 

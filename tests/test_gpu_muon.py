@@ -58,12 +58,12 @@ def test_newton_schulz_matches_oracle(prec, m, n, count, steps):
 def test_f32_tile_sizes_give_the_same_bits():
     """An fp32 launch with few jobs runs 64 x 64 tiles, a larger one 128 x 128.
     Both accumulate each output over k in the same order with the same MFMAs,
-    so a matrix iterated alone (3 Gram jobs at 128 x 128: the small tiles)
-    gives the bits it gets among 47 others (144 Gram jobs, 768 AXPY jobs: the
-    large tiles); the large-tile launch also meets the fp32 bar."""
+    so a 256 x 256 matrix iterated alone (3 Gram jobs at 128 x 128: the small
+    tiles; K = 256 is not split) gives the bits it gets among 47 others (144
+    Gram jobs: the large tiles); the large-tile launch also meets the fp32 bar."""
     import adamw_optimizer_step_amd as M
-    x0 = _x0(48, 256, 1024, 77, torch.float32)
-    say("ns f32 tiles: 48 matrices of 256x1024")
+    x0 = _x0(48, 256, 256, 77, torch.float32)
+    say("ns f32 tiles: 48 matrices of 256x256")
     many = to_np(M.newton_schulz(x0.to(DEV), KJ, 5))
     for k in (0, 47):
         say("ns f32 tiles: matrix", k, "alone")
@@ -71,6 +71,27 @@ def test_f32_tile_sizes_give_the_same_bits():
         assert bits_equal(alone, many[k]), first_mismatch(alone, many[k])
     ref = O.newton_schulz(to_np(x0[47]).astype(np.float64), KJ, "f64", 5)
     assert rel_fro(many[47], ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("m,n,slices", [(256, 1024, 4), (100, 300, 2), (384, 640, 3)])
+def test_f32_split_gram_matches_one_pass(m, n, slices):
+    """A small fp32 launch splits its Gram product along K (here into `slices`
+    slices of 256 columns) and adds the slices in order: the result differs
+    from one pass over K by fp32 summation order only. The same matrices
+    among enough others to take one pass must agree to 1e-5 relative, and
+    both meet the fp32 bar against the oracle."""
+    import adamw_optimizer_step_amd as M
+    count = 3 if m == 100 else 1
+    x0 = _x0(count, m, n, m + n + slices, torch.float32)
+    say("ns f32 split gram:", m, n, count)
+    split = to_np(M.newton_schulz(x0.to(DEV), KJ, 5))
+    pad = _x0(64, m, n, 5, torch.float32)   # 64 more matrices: no longer a small launch
+    one = to_np(M.newton_schulz(torch.cat([x0, pad]).to(DEV), KJ, 5))[:count]
+    for k in range(count):
+        assert rel_fro(split[k], one[k]) <= 1e-5, (k, rel_fro(split[k], one[k]))
+        ref = O.newton_schulz(to_np(x0[k]).astype(np.float64), KJ, "f64", 5)
+        assert rel_fro(split[k], ref) <= TOL["f32"]
+        assert rel_fro(one[k], ref) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
