@@ -134,6 +134,18 @@ NsTile ns_tile(int dtype, bool /*symmetric*/) {
 constexpr int kF32SmallLaunchJobs = 128;
 constexpr NsTile kF32SmallTile = {64, 64, 32, 2, 2, 0};
 
+// A bf16 Gram or POLY launch with fewer than this many 256 x 256 jobs (the
+// 4-layer d=256 set has 24) runs the register-staged kernel on 128 x 128
+// tiles, or on 64 x 64 ones under the fp32 rule above: a launch of a few long
+// LDS-DMA jobs lasts as long as one job's prologue, K loop and epilogue,
+// while the smaller tiles spread the same work over 4-16 times as many CUs.
+// POLY then writes B with its mirrored tiles, and the AXPY of the same
+// matrices reads B as stored (its transposed reads of the upper triangle
+// assume 256 x 256 blocks). AXPY itself keeps the LDS-DMA kernel, which reads
+// X^T out of X.
+constexpr int kBf16SmallLaunchJobs = 64;
+constexpr NsTile kBf16SmallTile = {128, 128, 32, 2, 2, 0};
+
 // Such a launch's Gram product (K = the long side, up to 4x the short one)
 // is also split along K into up to 4 slices of whole 256-column blocks, so
 // that its jobs x slices stay within this many blocks: each slice's partial
@@ -414,6 +426,18 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
       for (size_t base = 0; base < order.size(); base += kMaxNsGroups) {
         const size_t nb = std::min(order.size() - base, (size_t)kMaxNsGroups);
         NsTile tile = tile0;
+        // bf16: the symmetric products of this batch on the register-staged kernel
+        bool sym_reg = false;
+        if (tile0.dma) {
+          int64_t jobs = 0;
+          for (size_t q = 0; q < nb; ++q) {
+            const GroupPlan& p = plan.g[order[base + q]];
+            const int64_t tm = p.m_pad / tile0.bm;
+            jobs += p.count * tm * (tm + 1) / 2;
+          }
+          sym_reg = jobs < kBf16SmallLaunchJobs;
+          if (sym_reg && epi != EPI_AXPY) tile = kBf16SmallTile;
+        }
         if (!tile.dma) {
           int64_t jobs = 0;
           for (size_t q = 0; q < nb; ++q) {
@@ -451,7 +475,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.tm = G.tn = tm;
             G.tiles = tm * (tm + 1) / 2;
             G.symmetric = 1;
-            G.upper_only = epi == EPI_POLY && b_upper ? 1 : 0;
+            G.upper_only = epi == EPI_POLY && b_upper && !sym_reg ? 1 : 0;
           } else {
             G.P = ws + p.off_b;
             G.sP = p.a_stride;
@@ -475,7 +499,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             G.tn = tn;
             G.tiles = tm * tn;
             G.symmetric = 0;
-            G.p_upper = b_upper ? 1 : 0;
+            G.p_upper = b_upper && !sym_reg ? 1 : 0;
           }
           // the first GRAM and AXPY apply the deferred Frobenius factor
           const bool sc = step == 0 && epi != EPI_POLY && scaled && (*scaled)[order[base + q]];

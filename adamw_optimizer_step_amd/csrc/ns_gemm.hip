@@ -24,9 +24,10 @@
 //    are XOR-swizzled by row so that the fragment reads are conflict-free.
 //    Blocks are persistent, one per CU, each walking a fixed share of its
 //    XCD's tile list.
-//  * ns_gemm_reg (fp32): a register-staged double-buffered kernel,
-//    128 x 128 x 32 tiles of 2 x 2 waves on 32x32x2 fp32 MFMAs (64 x 64 x 32
-//    for launches with few jobs).
+//  * ns_gemm_reg: a register-staged double-buffered kernel, 128 x 128 x 32
+//    tiles of 2 x 2 waves (64 x 64 x 32 for launches with few jobs): every
+//    fp32 product on 32x32x2 fp32 MFMAs, and bf16 Gram and POLY launches of
+//    few jobs on 32x32x16 bf16 MFMAs.
 // Blocks are dealt to the 8 XCDs so that each XCD gets an eighth of every
 // shape group, whole matrices at a time where possible (see NsArgs).
 #include "ns_gemm.hpp"
@@ -1049,7 +1050,10 @@ static hipError_t launch_reg_epi(int epi, const NsArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_GRAM: return launch_reg<DT, EPI_GRAM, BM, BN, BK, WGM, WGN>(a, s);
     case EPI_POLY: return launch_reg<DT, EPI_POLY, BM, BN, BK, WGM, WGN>(a, s);
-    case EPI_AXPY: return launch_reg<DT, EPI_AXPY, BM, BN, BK, WGM, WGN>(a, s);
+    case EPI_AXPY:
+      // bf16 AXPY always runs the LDS-DMA kernel (it reads X^T out of X)
+      if constexpr (DT == DT_F32) return launch_reg<DT, EPI_AXPY, BM, BN, BK, WGM, WGN>(a, s);
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }
@@ -1131,8 +1135,16 @@ hipError_t launch_split_sum(const SplitSumArgs& a, hipStream_t s) {
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& a, hipStream_t s) {
   if (a.padded_blocks <= 0) return hipSuccess;
   if (dtype == DT_BF16) {
+    if (!tile.dma) {
+      // launches of few jobs (GRAM and POLY only): the register-staged kernel
+      constexpr int DTv = DT_BF16;
+      if (epi == EPI_AXPY || tile.qt) return hipErrorInvalidValue;
+      MA_REG_TILE(128, 128, 32, 2, 2)
+      MA_REG_TILE(64, 64, 32, 2, 2)
+      return hipErrorInvalidValue;
+    }
     // the LDS-DMA kernel, 256 x 256 x 64 tiles, 2 x 4 waves
-    if (!tile.dma || tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK || tile.wgm != 2 || tile.wgn != 4)
+    if (tile.bm != dma::BM || tile.bn != dma::BN || tile.bk != dma::BK || tile.wgm != 2 || tile.wgn != 4)
       return hipErrorInvalidValue;
     return launch_dma_epi<2, 4>(epi, tile.qt != 0, a, s);
   } else {

@@ -333,49 +333,70 @@ def graph_timing(torch, dev, step, n):
     return mean, per
 
 
+def _step_latency(M, torch, dev, wl, n, **hp_kw):
+    """Eager and graph-replay p10/median/p90 of one whole optimizer step of
+    workload ``wl`` (hyperparameters overridden by ``hp_kw``), in
+    microseconds."""
+    from workloads import materialize
+    data = materialize(wl, device=dev, seed=0)
+    groups = [M.MuonGroup(d["W"], d["G"], d["M"]) for d in data["muon"]]
+    kw = dict(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
+              ns_steps=wl.ns_steps, coeffs=M.KELLER_JORDAN, cautious=wl.cautious, equilibrate=wl.equilibrate,
+              ns_precision=wl.ns_precision, lr_scale=wl.lr_scale)
+    kw.update(hp_kw)
+    hp = M.MuonHParams(**kw)
+    ws = torch.empty(max(1, M.muon_workspace_size(groups, hp)), dtype=torch.uint8, device=dev)
+    segs = [dict(param=a["p"], grad=a["g"], exp_avg=a["m"], exp_avg_sq=a["v"], step=a["step"], lr=a["spec"].lr,
+                 beta1=a["spec"].beta1, beta2=a["spec"].beta2, eps=a["spec"].eps,
+                 weight_decay=a["spec"].weight_decay) for a in data["adamw"]]
+    step = lambda: M.optimizer_step(groups, hp, segs, workspace=ws, overlap=bool(segs))
+    for _ in range(10):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    eager = quantiles([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    _, per = graph_timing(torch, dev, step, n)
+    graph = quantiles(per)
+    del data, groups, ws, segs
+    torch.cuda.empty_cache()
+    return ([round(1e3 * v, 1) for v in eager], [round(1e3 * v, 1) for v in graph])
+
+
 def latency_lines(M, torch, dev, n):
     """Latency of one whole optimizer step on the two small configurations,
-    which launch and latency bound (they cannot fill 256 CUs): the single fp32
-    256 x 1024 matrix (5 steps of the fp32 iteration) and the 4-layer d=256 set
-    (bf16 Muon with AdamW beside it). Median and p10/p90 over ``n`` steps, eager
-    and as graph replays, in microseconds."""
-    from workloads import materialize, workload
+    which are launch and latency bound (they cannot fill 256 CUs): the single
+    fp32 256 x 1024 matrix (5 steps of the fp32 iteration; also swept over 1,
+    3 and 5 steps in fp32 and bf16 iteration) and the 4-layer d=256 set (bf16
+    Muon with AdamW beside it). Median and p10/p90 over ``n`` steps, eager and
+    as graph replays, in microseconds."""
+    from workloads import workload
     out = {}
     for name in ("c1_256x1024_f32", "c2_4L_d256"):
         wl = workload(name)
-        data = materialize(wl, device=dev, seed=0)
-        groups = [M.MuonGroup(d["W"], d["G"], d["M"]) for d in data["muon"]]
-        hp = M.MuonHParams(lr=wl.lr, momentum=wl.momentum, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
-                           ns_steps=wl.ns_steps, coeffs=M.KELLER_JORDAN, cautious=wl.cautious,
-                           equilibrate=wl.equilibrate, ns_precision=wl.ns_precision, lr_scale=wl.lr_scale)
-        ws = torch.empty(max(1, M.muon_workspace_size(groups, hp)), dtype=torch.uint8, device=dev)
-        segs = [dict(param=a["p"], grad=a["g"], exp_avg=a["m"], exp_avg_sq=a["v"], step=a["step"], lr=a["spec"].lr,
-                     beta1=a["spec"].beta1, beta2=a["spec"].beta2, eps=a["spec"].eps,
-                     weight_decay=a["spec"].weight_decay) for a in data["adamw"]]
-        step = lambda: M.optimizer_step(groups, hp, segs, workspace=ws, overlap=bool(segs))
-        for _ in range(10):
-            step()
-        stream = torch.cuda.current_stream(dev)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for i in range(n):
-            step()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        eager = quantiles([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
-        _, per = graph_timing(torch, dev, step, n)
-        graph = quantiles(per)
+        eager, graph = _step_latency(M, torch, dev, wl, n)
         out[name] = {"description": wl.description, "unit": "us",
-                     "eager_p10_median_p90": [round(1e3 * v, 1) for v in eager],
-                     "graph_p10_median_p90": [round(1e3 * v, 1) for v in graph],
+                     "eager_p10_median_p90": eager, "graph_p10_median_p90": graph,
                      "ns_gflop": round(wl.ns_steps * sum(g.count * (3 * min(g.rows, g.cols) ** 2 * max(g.rows, g.cols)
                                                                    + min(g.rows, g.cols) ** 3)
                                                           for g in wl.muon_groups) / 1e9, 3)}
-        del data, groups, ws, segs
-        torch.cuda.empty_cache()
-        print(f"[bench] latency {name}: eager {out[name]['eager_p10_median_p90'][1]} us, "
-              f"graph {out[name]['graph_p10_median_p90'][1]} us", file=sys.stderr, flush=True)
+        print(f"[bench] latency {name}: eager {eager[1]} us, graph {graph[1]} us", file=sys.stderr, flush=True)
+        if name.startswith("c1_"):
+            # the ns_steps sweep {1, 3, 5} of the same matrix, in both iteration precisions
+            sweep = {}
+            for prec in ("f32", "bf16"):
+                for t in (1, 3, 5):
+                    e, g = _step_latency(M, torch, dev, wl, n, ns_steps=t, ns_precision=prec)
+                    sweep[f"{prec}_T{t}"] = {"eager_p10_median_p90": e, "graph_p10_median_p90": g}
+            out[name]["sweep"] = sweep
+            print("[bench] latency c1 sweep (graph median, us): " +
+                  ", ".join(f"{k} {v['graph_p10_median_p90'][1]}" for k, v in sweep.items()), file=sys.stderr,
+                  flush=True)
     return out
 
 

@@ -28,8 +28,11 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# (rows, cols, count): wide, tall, and a padded odd shape of each orientation
-SHAPES = [(512, 1280, 3), (1280, 512, 3), (300, 700, 2), (700, 300, 2)]
+# (rows, cols, count): wide, tall, and a padded odd shape of each orientation;
+# 108 Gram jobs of 256 x 256, enough for the LDS-DMA kernel on every product
+# (a launch of fewer than 64 runs its Gram and POLY on the register-staged
+# kernel, which writes B with its mirrors)
+SHAPES = [(512, 1280, 12), (1280, 512, 12), (300, 700, 6), (700, 300, 6)]
 
 CHILD = r"""
 import hashlib, sys, torch

@@ -94,6 +94,27 @@ def test_f32_split_gram_matches_one_pass(m, n, slices):
         assert rel_fro(one[k], ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("m,n", [(256, 1024), (512, 512), (300, 700)])
+def test_bf16_small_and_large_launches(m, n):
+    """A bf16 Gram or POLY launch of fewer than 64 jobs of 256 x 256 runs the
+    register-staged kernel (POLY adding b A in its epilogue, B stored with its
+    mirrors); a larger one the LDS-DMA kernel (b A folded into the main loop,
+    B stored as its upper triangle). The same matrices alone and among 64
+    others (one launch of each form) both meet the bf16 bar against the
+    oracle's rounding points, and each other's."""
+    import adamw_optimizer_step_amd as M
+    x0 = _x0(2, min(m, n), max(m, n), m + 3 * n, torch.bfloat16)
+    say("ns bf16 small/large launch:", m, n)
+    small = to_np(M.newton_schulz(x0.to(DEV), KJ, 5))
+    pad = _x0(64, min(m, n), max(m, n), 9, torch.bfloat16)
+    large = to_np(M.newton_schulz(torch.cat([x0, pad]).to(DEV), KJ, 5))[:2]
+    for k in range(2):
+        ref = O.newton_schulz(to_np(x0[k]).astype(np.float64), KJ, "bf16", 5)
+        assert rel_fro(small[k], ref) <= TOL["bf16"], (k, rel_fro(small[k], ref))
+        assert rel_fro(large[k], ref) <= TOL["bf16"], (k, rel_fro(large[k], ref))
+        assert rel_fro(small[k], large[k]) <= TOL["bf16"], (k, rel_fro(small[k], large[k]))
+
+
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 def test_newton_schulz_special_coefficients(prec):
     """(1,0,0) copies X exactly; (0,1,0) gives X X^T X; (0,0,1) gives (X X^T)^2 X."""
