@@ -151,7 +151,8 @@ constexpr NsTile kBf16SmallTile = {128, 128, 32, 2, 2, 0};
 // that its jobs x slices stay within this many blocks: each slice's partial
 // product goes to a workspace buffer of its own, and k_split_sum adds the
 // slices in order (deterministic, but rounded differently from one pass over
-// K) and applies the deferred Frobenius factor.
+// K). An fp32 iterate is never stored before its Frobenius factor (the
+// one-pass X0 is bf16 only), so there is no factor to apply to the sum.
 constexpr int kF32SplitMaxBlocks = 256;
 
 // Slices for an fp32 group's Gram product when launched alone: 1 (no split)
@@ -537,7 +538,7 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
           }
           if (split < 2 || (int)nb * split > kMaxNsGroups || jobs * split > kF32SplitMaxBlocks) split = 1;
           for (size_t q = 0; q < nb && split > 1; ++q)
-            if ((A.g[q].K / 256) % split) split = 1;
+            if ((A.g[q].K / 256) % split || A.g[q].scale) split = 1;
         }
         if (split > 1) {
           NsArgs S = A;
@@ -552,7 +553,6 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
               G.K = kc;
               void* part = ws + p.off_gpart + (size_t)sl * p.count * p.a_stride * e;
               G.outN = G.outT = part;
-              G.scale = nullptr;   // applied to the sum
               G.rot = rot;
               rot = (rot + G.count * G.tiles / G.unit) & 7;
               S.g[k] = G;
@@ -593,9 +593,6 @@ int enqueue_ns(const Plan& plan, unsigned char* ws, const float* abc, int T, int
             g.split_stride = (int64_t)p.count * p.a_stride;
             g.mat_elems = p.a_stride;
             g.slices = split;
-            const bool sc = step == 0 && scaled && (*scaled)[order[base + q]];
-            g.scale = sc ? reinterpret_cast<const float*>(ws + p.off_rowf) : nullptr;
-            g.scale_stride = p.row_stride;
             g.block_begin = blocks;
             blocks += g.split_stride / kSplitSumBlockElems;
           }

@@ -1112,15 +1112,6 @@ __global__ void __launch_bounds__(256) k_split_sum(const SplitSumArgs a) {
     v.z = __fadd_rn(v.z, w.z);
     v.w = __fadd_rn(v.w, w.w);
   }
-  if (g.scale) {
-    // the Gram product of X = s Y is s^2 Y Y^T, as in the unsplit epilogue
-    float sc = g.scale[(i / g.mat_elems) * g.scale_stride];
-    sc = sc * sc;
-    v.x *= sc;
-    v.y *= sc;
-    v.z *= sc;
-    v.w *= sc;
-  }
   *reinterpret_cast<float4*>(g.out + i) = v;
 }
 

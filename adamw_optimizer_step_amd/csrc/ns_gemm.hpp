@@ -84,16 +84,13 @@ struct NsTile { int bm, bn, bk, wgm, wgn, dma, qt = 0; };
 hipError_t launch_ns_gemm(int dtype, int epi, NsTile tile, const NsArgs& args, hipStream_t s);
 
 // Sum of the K slices of a split fp32 Gram product (k_split_sum): per group,
-// out[i] = (part_0[i] + part_1[i] + ...) in slice order, times the matrix's
-// deferred Frobenius factor squared when `scale` is set, over count matrices
+// out[i] = (part_0[i] + part_1[i] + ...) in slice order, over count matrices
 // of mat_elems floats (a multiple of kSplitSumBlockElems). Blocks
 // block_begin .. of the launch belong to the group.
 constexpr int kSplitSumBlockElems = 1024;   // 256 threads x 4 floats
 struct SplitSumGroup {
   const float* part;
   float* out;
-  const float* scale;
-  int64_t scale_stride;     // floats between matrices' factors
   int64_t mat_elems;        // floats per matrix
   int64_t split_stride;     // floats between slices (count x mat_elems)
   int64_t block_begin;
