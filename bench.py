@@ -407,24 +407,29 @@ def practical_peaks(L, lib, dev):
     operands and on random operands that change every MFMA (the part is power
     limited: the second draws more power and runs at a lower clock, which is
     the ceiling for products of real data), and a plain 1 GiB fp32 copy
-    (torch.neg: 1 GiB read, 1 GiB written)."""
+    (torch.neg: 1 GiB read, 1 GiB written). Each MFMA figure is the steady
+    state: about 0.25 s of launches to let the clock settle (a few launches
+    straight from idle read 6-10% low), then 100 launches (about 0.25 s)
+    timed."""
     import ctypes as C
     import torch
     stream = torch.cuda.current_stream(dev)
-    blocks, iters = 1024, 2048
+    blocks, iters, timed = 1024, 2048, 100
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     mfma = {}
     for changing in (0, 1):
-        L.check(lib.ma_calib_mfma(blocks, iters, changing, C.c_void_p(sink.data_ptr()), C.c_void_p(stream.cuda_stream)))
+        for _ in range(timed):
+            L.check(lib.ma_calib_mfma(blocks, iters, changing, C.c_void_p(sink.data_ptr()),
+                                      C.c_void_p(stream.cuda_stream)))
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(3):
+        for _ in range(timed):
             L.check(lib.ma_calib_mfma(blocks, iters, changing, C.c_void_p(sink.data_ptr()),
                                       C.c_void_p(stream.cuda_stream)))
         e1.record(stream)
         torch.cuda.synchronize()
-        mfma[changing] = 3 * blocks * 4 * iters * 16 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        mfma[changing] = timed * blocks * 4 * iters * 16 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     n = 1 << 28
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
