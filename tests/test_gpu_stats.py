@@ -7,7 +7,13 @@
 * ||W_new - W_old|| must match the oracle's step: to 1e-3 with ns_steps = 0
   (the update is X0, whose bf16 rounding can differ in a few elements: the
   kernels normalise in fp32, the oracle in float64) and to the bf16
-  iteration's bound with five steps.
+  iteration's bar of 2e-2 with five steps. The step is c_lr U plus the masked
+  decay c_wd W, so | ||dW_gpu|| - ||dW_oracle|| | <= c_lr ||U_gpu - U_oracle||
+  + c_wd ||W|| over the elements where the cautious masks differ; the first
+  term is within 2e-2 of c_lr ||U|| by the iteration's bar, and the second is
+  below 1e-5 of the step here (c_wd |W| ~ 4e-6 against steps ~ 1e-3, on the
+  few elements where u w changes sign). Rounding W_new to bf16 changes the
+  norm only to second order (about (2^-9 |W| / |dW|)^2 ~ 1e-3 relative).
 Shapes cover the vector path (rows a multiple of 8) and the tile path (odd
 columns), bf16 and fp32 weights, wide, square and tall matrices.
 
@@ -72,11 +78,11 @@ def _gpu():
     need_gpu()
 
 
-@pytest.mark.parametrize("ns_steps,tol", [(0, 1e-3), (5, 3e-2)])
+@pytest.mark.parametrize("ns_steps,tol", [(0, 1e-3), (5, 2e-2)])
 def test_stats_against_the_oracle(ns_steps, tol):
     say("stats: ns_steps", ns_steps)
     host, dev, hp, st = _run(ns_steps, seed=11 + ns_steps)
-    k = 0
+    k, worst = 0, 0.0
     for (W, G, Mo, pdt), d in zip(host, dev):
         for i in range(W.shape[0]):
             r = _oracle(W[i], G[i], Mo[i], pdt, hp, ns_steps)
@@ -87,7 +93,9 @@ def test_stats_against_the_oracle(ns_steps, tol):
             assert abs(st[k, 1] - wn) <= 1e-5 * wn, (k, st[k], wn)
             assert abs(st[k, 0] - dn_own) <= 1e-5 * dn_own, (k, st[k], dn_own)
             assert abs(st[k, 0] - dn_ora) <= tol * dn_ora, (k, st[k], dn_ora)
+            worst = max(worst, abs(st[k, 0] - dn_ora) / dn_ora)
             k += 1
+    say("stats: largest relative step-norm difference from the oracle", f"{worst:.2e}")
 
 
 def test_stats_step_writes_the_same_weights():
