@@ -192,7 +192,7 @@ template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false
           bool UPD = false>
 __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
                                             f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
-                                            unsigned char* smem, int tid_in = -1) {
+                                            unsigned char* smem, int tid_in = -1, bool mirror_lower = false) {
   using Tr = MfmaTraits<DT>;
   using T = typename Tr::T;
   using ES = EpiSmem<DT, BM, BN>;
@@ -355,6 +355,27 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
           }
         }
       }
+    if constexpr (ACC_T && BM == BN && DT == DT_BF16) {
+      if (mirror_lower && diag) {
+        // rows BM/2.., columns ..BN/2 were not computed (their waves skipped
+        // the K loop): they are the transpose of rows ..BM/2, columns BN/2..
+        // (computed, they would hold the same sums of the same products with
+        // the MFMA operands swapped, equal to those up to fp32 rounding; the
+        // mirror makes the diagonal tile exactly symmetric). Each thread
+        // moves 8 values: one 16-byte read along a row above the diagonal, 8
+        // two-byte writes down a column below it.
+        __syncthreads();
+        constexpr int H = BM / 2, CH = H / 8;
+#pragma unroll
+        for (int u = 0; u < H * CH / NT; ++u) {
+          const int idx = tid + NT * u, cc = idx % H, rc = idx / H;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + cc * ES::LDN + H + rc * 8);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) stg[(H + rc * 8 + e) * ES::LDN + cc] = (T)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
     T* dst = outN + (int64_t)mat * G.sN + (int64_t)(bi * BM) * G.ldN + bj * BN;
     constexpr int CPR = BN / VEC;
     constexpr int NU = BM * CPR / NT;
@@ -856,6 +877,30 @@ __device__ __forceinline__ void dma_kstep(const DmaCtx& c, int kt,
   }
 }
 
+// The k-loop of a wave whose output blocks all lie below the diagonal of a
+// diagonal tile of a symmetric product: it keeps its part of the pipeline
+// (its DMA share of every k-tile, the same waits and block barriers as the
+// computing waves) but reads no fragments and issues no MFMAs; the epilogue
+// fills its blocks from the transposed blocks above the diagonal.
+template <int WGM, int WGN>
+__device__ __forceinline__ void dma_skip_ktiles(const DmaCtx& c) {
+  using namespace dma;
+  constexpr int DPW = Grid<WGM, WGN>::DPW;
+  for (int kt = 0; kt < c.nk; ++kt) {
+    if (kt + 1 < c.nk) {
+      const int later = c.nk - 2 - kt;
+      dma_wait_tiles<DPW>(later < STAGES - 2 ? later : STAGES - 2);
+      __builtin_amdgcn_s_barrier();
+    }
+    if (kt + STAGES < c.nk) {
+      unsigned char* fill_at = c.wave_fill + (kt % STAGES) * STAGE_BYTES;
+      const int lo[2] = {c.lane_off[0], c.lane_off[1]};
+#pragma unroll
+      for (int q = 0; q < DPW; ++q) dma_issue_one(fill_at, c.src, c.q_step, lo, (int64_t)(kt + STAGES) * c.k_step, q);
+    }
+  }
+}
+
 // One k-tile: KK k-steps, the fragment sets alternating (0, 1) -> (1, 0) -> ...
 // so that (f0a, f0b) again hold the next tile's first k-step afterwards.
 template <int IIB, int WGM, int WGN, bool QT, bool PT = false>
@@ -981,6 +1026,16 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   }
   dma_wait_tiles<DPW>(STAGES - 1);   // this wave's part of tile 0 has landed
   __builtin_amdgcn_s_barrier();
+  // a diagonal tile of a symmetric product: the waves whose blocks all lie
+  // below the diagonal (rows 128..255, columns 0..127) compute nothing
+  const bool mirror_lower = !QT && G.symmetric && J.bi == J.bj;
+  if (mirror_lower && c.wm * Gd::WTM >= BM / 2 && (c.wn + 1) * Gd::WTN <= BN / 2) {
+    static_assert(QT || BM == BN, "square tiles");
+    dma_skip_ktiles<WGM, WGN>(c);
+    __syncthreads();
+    ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true, UPD>(args, G, J, acc, smem, tid, true);
+    return;
+  }
   u32x4_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
   int kt = 0;
   if constexpr (QT) {
@@ -1007,7 +1062,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
   __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true, UPD>(args, G, J, acc, smem, tid);
+  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true, UPD>(args, G, J, acc, smem, tid, mirror_lower);
 }
 
 // Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
