@@ -23,7 +23,8 @@
 //    VGPR staging), one tile ahead of the one being multiplied; 16-byte chunks
 //    are XOR-swizzled by row so that the fragment reads are conflict-free.
 //    Blocks are persistent, one per CU, each walking a fixed share of its
-//    XCD's tile list.
+//    XCD's tile list. In a diagonal tile of GRAM or POLY the two waves below
+//    the diagonal skip the K loop; the epilogue mirrors their quadrant.
 //  * ns_gemm_reg: a register-staged double-buffered kernel, 128 x 128 x 32
 //    tiles of 2 x 2 waves (64 x 64 x 32 for launches with few jobs): every
 //    fp32 product on 32x32x2 fp32 MFMAs, and bf16 Gram and POLY launches of
@@ -555,10 +556,9 @@ ns_gemm_reg(const NsArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-DMA kernel (bf16): 256 x 256 x BK tiles, WGM x WGN waves (2 x 2 of
-// 128 x 128, one wave per SIMD; or 2 x 4 of 128 x 64, two waves per SIMD so
-// that one wave's fragment reads and waits overlap the other's MFMAs), a ring
-// of STAGES k-tiles in LDS
+// LDS-DMA kernel (bf16): 256 x 256 x BK tiles, 2 x 4 waves of 128 x 64, two
+// per SIMD so that one wave's fragment reads and waits overlap the other's
+// MFMAs, a ring of STAGES k-tiles in LDS
 // ---------------------------------------------------------------------------
 namespace dma {
 constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;

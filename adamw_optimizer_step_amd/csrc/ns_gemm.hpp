@@ -75,7 +75,7 @@ struct NsArgs {
 constexpr int kNsPersBlocksPerXcd = 32;   // CUs per XCD
 
 // tile configuration chosen per launch: block tile bm x bn, K tile bk,
-// wgm x wgn waves; dma selects the LDS-DMA kernel (bf16, 256 x 256 x BK, 2 x 2 or 2 x 4 waves);
+// wgm x wgn waves; dma selects the LDS-DMA kernel (bf16, 256 x 256 x BK, 2 x 4 waves);
 // qt (AXPY, 2 x 4 waves): Q = X^T is read from X (row-major) through
 // transposing LDS reads, so the iteration needs no X^T copy
 struct NsTile { int bm, bn, bk, wgm, wgn, dma, qt = 0; };
@@ -103,7 +103,7 @@ struct SplitSumArgs {
 };
 hipError_t launch_split_sum(const SplitSumArgs& args, hipStream_t s);
 
-// k-tile of the LDS-DMA kernel (its block tile is 256 x 256, 2 x 2 waves)
+// k-tile of the LDS-DMA kernel (its block tile is 256 x 256, 2 x 4 waves)
 int ns_dma_bk();
 
 }  // namespace ma

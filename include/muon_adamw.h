@@ -143,8 +143,9 @@ typedef struct {
 /* Bytes of device workspace ma_muon_step needs for these groups and
  * hyperparameters (0 on invalid arguments; see ma_last_error). The
  * workspace holds the normalised momentum and the Newton-Schulz iterates
- * and Gram matrices of every matrix, padded to multiples of 256, and the
- * partial sums of ma_muon_step_stats. */
+ * and Gram matrices of every matrix, padded to multiples of 256, the
+ * partial sums of ma_muon_step_stats and, for fp32 groups small enough that
+ * their Gram product is split along K, its per-slice partial products. */
 size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
                               const ma_muon_hparams* hp);
 
@@ -168,7 +169,12 @@ size_t ma_muon_workspace_size(const ma_muon_group* groups, int32_t n_groups,
  * workspace: DEVICE, >= ma_muon_workspace_size bytes, MA_WORKSPACE_ALIGN
  * aligned. Parameter, gradient and momentum buffers must not overlap each
  * other or the workspace (MA_ERR_INVALID_ARG is returned for overlaps among
- * the pointers passed). */
+ * the pointers passed).
+ * Results are deterministic for given inputs. The kernels a call uses depend
+ * on its total work (launches of few tile jobs run smaller tiles, and an fp32
+ * Gram product of few jobs is split along K), so one matrix stepped alone
+ * and the same matrix stepped with many others can differ at the rounding
+ * level. */
 int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp,
                  void* workspace, size_t workspace_bytes, void* stream);
 
