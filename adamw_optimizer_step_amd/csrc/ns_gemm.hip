@@ -360,9 +360,10 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
       if (mirror_lower && diag) {
         // rows BM/2.., columns ..BN/2 were not computed (their waves skipped
         // the K loop): they are the transpose of rows ..BM/2, columns BN/2..
-        // (computed, they would hold the same sums of the same products with
-        // the MFMA operands swapped, equal to those up to fp32 rounding; the
-        // mirror makes the diagonal tile exactly symmetric). Each thread
+        // (computed, they would hold the same products, equal to these up to
+        // fp32 rounding: in POLY the folded term enters the two quadrants'
+        // sums at different k-tiles; the mirror makes the diagonal tile
+        // exactly symmetric). Each thread
         // moves 8 values: one 16-byte read along a row above the diagonal, 8
         // two-byte writes down a column below it.
         __syncthreads();
