@@ -921,8 +921,20 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
 // is added inside the main loop by scaled-identity MFMAs against the Q
 // fragments, so the epilogue reads nothing back from global memory. AXPY
 // always folds.
+// Job slot in LDS: the block's next job (gi, mat, bi, bj; gi < 0: none),
+// written by wave 0 while its first operand DMA is in flight
+__device__ __forceinline__ void put_job(int* slot, bool ok, const TileJob& N) {
+  slot[0] = ok ? N.gi : -1;
+  slot[1] = N.mat;
+  slot[2] = N.bi;
+  slot[3] = N.bj;
+}
+
+// next_slot (optional): where wave 0 stores job `next_local` of XCD `xcd`'s
+// list, so that the other waves need not map it
 template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD>
-__device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem) {
+__device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem,
+                                         int xcd = 0, int next_local = 0, int* next_slot = nullptr) {
   using namespace dma;
   using Gd = Grid<WGM, WGN>;
   constexpr int FM = Gd::FM, FN = Gd::FN, DPW = Gd::DPW, NW = Gd::NW;
@@ -1025,6 +1037,12 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
     else
       dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.q_step, c.lane_off, (int64_t)t * c.k_step);
   }
+  if (next_slot && wave == 0) {
+    // the next job's (scalar) mapping, while the first k-tiles land
+    TileJob N;
+    const bool ok = map_job_at(args, xcd, next_local, N);
+    if (lane == 0) put_job(next_slot, ok, N);
+  }
   dma_wait_tiles<DPW>(STAGES - 1);   // this wave's part of tile 0 has landed
   __builtin_amdgcn_s_barrier();
   // a diagonal tile of a symmetric product: the waves whose blocks all lie
@@ -1078,16 +1096,30 @@ template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD>
 __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 ns_gemm_dma(const NsArgs args) {
   using namespace dma;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES];
+  // one LDS object (see above): the two job slots follow the operand ring /
+  // epilogue staging
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[BYTES + 32];
+  int* const slots = reinterpret_cast<int*>(smem + BYTES);
   // issue priority over waves of other kernels sharing the CU (the AdamW
   // update that may run beside the iteration on another stream, at priority 0)
   __builtin_amdgcn_s_setprio(1);
   const int x = (int)(blockIdx.x & 7);
   const int P = (int)(gridDim.x >> 3);
   TileJob J;
-  for (int local = (int)(blockIdx.x >> 3); map_job_at(args, x, local, J); local += P) {
-    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD>(args, J, smem);
+  int local = (int)(blockIdx.x >> 3);
+  bool have = map_job_at(args, x, local, J);
+  // job j's successor goes to slot (j + 1) & 1: a slot is rewritten two jobs
+  // later, after every wave has passed the barrier that follows its reads
+  for (int j = 0; have; ++j) {
+    int* const slot = slots + 4 * ((j + 1) & 1);
+    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD>(args, J, smem, x, local + P, slot);
     __syncthreads();   // the epilogue is done with LDS before the next job's DMA
+    local += P;
+    have = slot[0] >= 0;
+    J.gi = slot[0];
+    J.mat = slot[1];
+    J.bi = slot[2];
+    J.bj = slot[3];
   }
 }
 
