@@ -235,6 +235,11 @@ void plan_group(GroupPlan& p, int64_t R, int64_t C, int count, int dt_x, size_t&
   if (p.gram_split > 1) off = align_up(off + (size_t)p.gram_split * count * p.a_stride * 4, MA_WORKSPACE_ALIGN);
 }
 
+// Largest Muon group (count x rows x cols) and flat AdamW / Lion segment, in
+// elements: 2^40 is 2 TiB of bf16, far beyond one GPU's memory.
+constexpr int64_t kMaxGroupElems = (int64_t)1 << 40;
+constexpr int64_t kMaxSegmentElems = (int64_t)1 << 40;
+
 int validate_hparams(const ma_muon_hparams* hp) {
   if (!hp) return fail(MA_ERR_INVALID_ARG, "hparams is null");
   if (hp->ns_steps < 0 || hp->ns_steps > MA_MAX_NS_STEPS)
@@ -286,6 +291,9 @@ int validate_group(const ma_muon_group& g, int idx, bool need_ptrs) {
     return fail(MA_ERR_INVALID_ARG, "group %d: rows/cols must be > 0 and count >= 0", idx);
   if (g.rows > (1 << 24) || g.cols > (1 << 24) || g.rows * g.cols > (int64_t)1 << 31)
     return fail(MA_ERR_INVALID_ARG, "group %d: matrix too large", idx);
+  // keeps every tile-job count and launch size of the group within int32
+  if ((int64_t)g.count * g.rows * g.cols > kMaxGroupElems)
+    return fail(MA_ERR_INVALID_ARG, "group %d: more than 2^40 elements in all", idx);
   if (!dt_valid(g.param_dtype) || !dt_valid(g.grad_dtype) || !dt_valid(g.mom_dtype))
     return fail(MA_ERR_UNSUPPORTED, "group %d: dtype must be MA_F32 or MA_BF16", idx);
   if (need_ptrs && g.count > 0) {
@@ -1048,7 +1056,7 @@ int adamw_prepare(const ma_adamw_segment* segs, int32_t n, std::vector<Range>& r
   if (n < 0 || (n > 0 && !segs)) return fail(MA_ERR_INVALID_ARG, "segments is null or n < 0");
   for (int i = 0; i < n; ++i) {
     const ma_adamw_segment& S = segs[i];
-    if (S.n < 0) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0", i);
+    if (S.n < 0 || S.n > kMaxSegmentElems) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0 or n > 2^40", i);
     if (S.param_dtype != MA_F32 || S.grad_dtype != MA_F32)
       return fail(MA_ERR_UNSUPPORTED, "segment %d: AdamW buffers must be MA_F32", i);
     if (S.n == 0) continue;
@@ -1222,7 +1230,7 @@ int ma_lion_step(const ma_lion_segment* segs, int32_t n, void* stream) {
   std::vector<Range> rs;
   for (int i = 0; i < n; ++i) {
     const ma_lion_segment& S = segs[i];
-    if (S.n < 0) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0", i);
+    if (S.n < 0 || S.n > kMaxSegmentElems) return fail(MA_ERR_INVALID_ARG, "segment %d: n < 0 or n > 2^40", i);
     if (S.param_dtype != MA_F32 || S.grad_dtype != MA_F32)
       return fail(MA_ERR_UNSUPPORTED, "segment %d: Lion buffers must be MA_F32", i);
     if (S.n == 0) continue;

@@ -89,7 +89,9 @@ typedef enum {
 /* One group: `count` matrices of identical shape rows x cols.
  * params/grads/momentum are HOST arrays of `count` DEVICE pointers; matrix i
  * of the group is params[i] (rows*cols elements of param_dtype), grads[i]
- * (grad_dtype, read only) and momentum[i] (mom_dtype, updated in place). */
+ * (grad_dtype, read only) and momentum[i] (mom_dtype, updated in place).
+ * Limits (MA_ERR_INVALID_ARG beyond them): rows, cols <= 2^24,
+ * rows*cols <= 2^31, count*rows*cols <= 2^40. */
 typedef struct {
   int64_t rows, cols;
   int32_t count;
@@ -265,7 +267,7 @@ typedef struct {
  * Step-dependent scalars are formed in fp64 on the host and rounded to fp32
  * once; each per-element operation is one correctly rounded fp32 operation
  * (no fused multiply-add). Segments may be in any order and of any length
- * (n >= 0); buffers of different segments must not overlap.
+ * (0 <= n <= 2^40); buffers of different segments must not overlap.
  * `segments` is a HOST array. */
 int ma_adamw_step(const ma_adamw_segment* segments, int32_t n_segments, void* stream);
 
@@ -319,7 +321,7 @@ typedef struct {
  * rounded to fp32 once; each per-element operation is one correctly rounded
  * fp32 operation (no fused multiply-add). Requirements: finite lr and
  * weight_decay, 0 <= beta1, beta2 < 1. Segments may be in any order and of
- * any length (n >= 0); no two buffers, of one segment or of different
+ * any length (0 <= n <= 2^40); no two buffers, of one segment or of different
  * segments, may overlap. `segments` is a HOST array. Returns
  * MA_ERR_INVALID_ARG / MA_ERR_UNSUPPORTED before any launch on a bad
  * segment. */

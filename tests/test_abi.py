@@ -131,6 +131,15 @@ def test_muon_step_rejects_bad_arguments(mut, code):
     assert L.lib().ma_last_error()
 
 
+def test_muon_step_rejects_groups_beyond_the_size_bound():
+    # 1025 matrices of 2^15 x 2^15: each allowed, more than 2^40 elements in all
+    g, keep = group(rows=1 << 15, cols=1 << 15, count=1025)
+    h, tab = hp()
+    assert call_step(g, h) == L.MA_ERR_INVALID_ARG
+    assert b"2^40" in L.lib().ma_last_error()
+    assert L.lib().ma_muon_workspace_size((L.MuonGroupC * 1)(g), 1, C.byref(h)) == 0
+
+
 def test_muon_step_rejects_null_matrix_pointer():
     g, (p, gg, m) = group()
     gg[1] = None
@@ -193,6 +202,7 @@ def seg(**kw):
     (dict(grad=None), L.MA_ERR_INVALID_ARG),
     (dict(param=BASE + 2), L.MA_ERR_INVALID_ARG),
     (dict(exp_avg=BASE + 400), L.MA_ERR_INVALID_ARG),     # overlaps param
+    (dict(n=(1 << 40) + 1), L.MA_ERR_INVALID_ARG),        # beyond the size bound
 ])
 def test_adamw_rejects_bad_arguments(kw, code):
     arr = (L.AdamWSegmentC * 1)(seg(**kw))
@@ -334,6 +344,7 @@ def lseg(**kw):
     (dict(exp_avg=None), L.MA_ERR_INVALID_ARG),
     (dict(grad=BASE + (1 << 30) + 2), L.MA_ERR_INVALID_ARG),
     (dict(grad=BASE + 3996), L.MA_ERR_INVALID_ARG),          # overlaps param's last element
+    (dict(n=(1 << 40) + 1), L.MA_ERR_INVALID_ARG),           # beyond the size bound
 ])
 def test_lion_rejects_bad_arguments(kw, code):
     arr = (L.LionSegmentC * 1)(lseg(**kw))
