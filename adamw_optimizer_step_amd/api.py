@@ -91,6 +91,32 @@ def _matrix_ptrs(x: Union[torch.Tensor, Sequence[torch.Tensor]], rows: int, cols
     return out
 
 
+def _flat(x):
+    if x is None:
+        return []
+    if isinstance(x, torch.Tensor):
+        return [x]
+    return [t for t in x if t is not None]
+
+
+def _check_cuda(tensors, dev: torch.device, what: str):
+    """Every tensor a launch reads or writes lives on the GPU `dev`: the
+    library takes raw device pointers, so a host or other-GPU tensor would
+    reach a kernel as a bad address."""
+    if dev.type != "cuda":
+        raise ValueError(f"{what}: expected CUDA tensors, got a tensor on {dev}")
+    for t in tensors:
+        if t.device != dev:
+            raise ValueError(f"{what}: every tensor must be on {dev}, got one on {t.device}")
+
+
+def _check_groups(groups) -> torch.device:
+    dev = groups[0].device
+    for g in groups:
+        _check_cuda([t for x in g._keep for t in _flat(x)], dev, "Muon groups")
+    return dev
+
+
 def _check_dense(g):
     if g.layout != torch.strided:
         # as an optimizer's step() does for sparse gradients ("3.9 Optimizers",
@@ -183,10 +209,11 @@ def muon_step(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: Optional[
     written to it (``ma_muon_step_stats``)."""
     if not groups:
         return workspace
-    dev = groups[0].device
+    dev = _check_groups(groups)
     need = muon_workspace_size(groups, hp)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_cuda([workspace] + ([stats] if stats is not None else []), dev, "workspace and stats")
     garr, keep = _groups_c(groups)
     h, tab = hp.to_c()
     ws, st = C.c_void_p(workspace.data_ptr()), C.c_void_p(_stream(dev, stream))
@@ -208,6 +235,7 @@ def muon_step_noalloc(groups: Sequence[MuonGroup], hp: MuonHParams, stream=None)
     calls that overlap on one GPU must be ordered by the caller."""
     if not groups:
         return
+    _check_groups(groups)
     garr, keep = _groups_c(groups)
     h, tab = hp.to_c()
     L.check(L.lib().ma_muon_step_noalloc(garr, len(groups), C.byref(h), C.c_void_p(_stream(groups[0].device, stream))))
@@ -284,6 +312,8 @@ def adamw_step(segments: Sequence[dict], stream=None, workgroups: Optional[int] 
         return
     arr, n = _adamw_c(segments)
     dev = segments[0]["param"].device
+    _check_cuda([s[k] for s in segments if s["grad"] is not None for k in ("param", "grad", "exp_avg", "exp_avg_sq")],
+                dev, "AdamW buffers")
     if workgroups is None:
         L.check(L.lib().ma_adamw_step(arr, n, C.c_void_p(_stream(dev, stream))))
     else:
@@ -313,10 +343,12 @@ def optimizer_step(groups: Sequence[MuonGroup], hp: MuonHParams, adamw_segments:
         ws = muon_step(groups, hp, workspace=workspace)
         adamw_step(adamw_segments)
         return ws
-    dev = groups[0].device
+    dev = _check_groups(groups)
     need = muon_workspace_size(groups, hp)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_cuda([workspace] + [s[k] for s in adamw_segments if s["grad"] is not None
+                               for k in ("param", "grad", "exp_avg", "exp_avg_sq")], dev, "workspace and AdamW buffers")
     side = _SIDE.get(dev)
     if side is None:
         side = _SIDE[dev] = torch.cuda.Stream(device=dev)
@@ -336,6 +368,7 @@ def lion_step(segments: Sequence[dict], stream=None) -> None:
         return
     arr = (L.LionSegmentC * len(segments))()
     dev = segments[0]["param"].device
+    _check_cuda([s[k] for s in segments for k in ("param", "grad", "exp_avg")], dev, "Lion buffers")
     for i, s in enumerate(segments):
         p, g, m = s["param"], s["grad"], s["exp_avg"]
         for t in (p, g, m):
@@ -352,6 +385,7 @@ def lion_step(segments: Sequence[dict], stream=None) -> None:
 # ---------------------------------------------------------------------------
 
 def bf16_round(x: torch.Tensor, stream=None) -> torch.Tensor:
+    _check_cuda([x], x.device, "bf16_round")
     out = torch.empty(x.numel(), dtype=torch.int16, device=x.device)
     L.check(L.lib().ma_test_bf16_round(C.c_void_p(x.data_ptr()), C.c_void_p(out.data_ptr()), x.numel(),
                                        C.c_void_p(_stream(x.device, stream))))
@@ -359,6 +393,7 @@ def bf16_round(x: torch.Tensor, stream=None) -> torch.Tensor:
 
 
 def momentum_stage(group: MuonGroup, beta: float, nesterov: bool, stream=None) -> torch.Tensor:
+    _check_groups([group])
     mt = torch.empty((group.count, group.rows, group.cols), dtype=torch.float32, device=group.device)
     s, keep = group.to_c()
     L.check(L.lib().ma_test_muon_momentum(C.byref(s), beta, int(nesterov), C.c_void_p(mt.data_ptr()),
@@ -370,6 +405,7 @@ def update_stage(group: MuonGroup, u: torch.Tensor, c_lr: float, c_wd: float, ca
                  stream=None) -> None:
     if not u.is_contiguous():
         raise ValueError("u must be contiguous")
+    _check_cuda([u], _check_groups([group]), "update_stage")
     s, keep = group.to_c()
     L.check(L.lib().ma_test_muon_update(C.byref(s), C.c_void_p(u.data_ptr()), _dt(u), c_lr, c_wd,
                                         int(cautious), int(decay), C.c_void_p(_stream(group.device, stream))))
@@ -380,6 +416,7 @@ def newton_schulz(x0: torch.Tensor, coeffs, ns_steps: int, stream=None) -> torch
     if x0.dim() == 2:
         x0 = x0.unsqueeze(0)
     x0 = x0.contiguous()
+    _check_cuda([x0], x0.device, "newton_schulz")
     count, m, n = x0.shape
     prec = _dt(x0)
     tab = MuonHParams(ns_steps=ns_steps, coeffs=coeffs).table()

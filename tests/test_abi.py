@@ -292,6 +292,29 @@ def test_check_finite_field_and_query_validate():
     assert h1.check_finite == 1
 
 
+def test_launching_calls_reject_host_tensors():
+    """The binding refuses, before any library call, tensors that are not on
+    the GPU: the kernels would get host addresses."""
+    import torch
+    from adamw_optimizer_step_amd import api
+    W = torch.zeros(2, 8, 16, dtype=torch.bfloat16)
+    grp = api.MuonGroup(W, torch.zeros_like(W), torch.zeros_like(W))
+    hp = api.MuonHParams(ns_steps=1)
+    for call in (lambda: api.muon_step([grp], hp), lambda: api.muon_step_noalloc([grp], hp),
+                 lambda: api.momentum_stage(grp, 0.9, True), lambda: api.newton_schulz(W[0].float(), api.KELLER_JORDAN, 1),
+                 lambda: api.bf16_round(torch.zeros(4))):
+        with pytest.raises(ValueError, match="CUDA"):
+            call()
+    p = torch.zeros(8)
+    seg = dict(param=p, grad=torch.zeros(8), exp_avg=torch.zeros(8), exp_avg_sq=torch.zeros(8), lr=1e-3, step=1)
+    with pytest.raises(ValueError, match="CUDA"):
+        api.adamw_step([seg])
+    with pytest.raises(ValueError, match="CUDA"):
+        api.lion_step([dict(param=p, grad=torch.zeros(8), exp_avg=torch.zeros(8), lr=1e-3)])
+    with pytest.raises(ValueError, match="CUDA"):
+        api.optimizer_step([grp], hp, [seg])
+
+
 def test_missing_gradients_are_left_out_and_sparse_ones_rejected():
     """The wrapper drops matrices and AdamW buffers whose gradient is None
     (CPU tensors: only pointers are taken, nothing is launched)."""
