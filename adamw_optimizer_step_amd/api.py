@@ -235,10 +235,11 @@ def muon_step_noalloc(groups: Sequence[MuonGroup], hp: MuonHParams, stream=None)
     calls that overlap on one GPU must be ordered by the caller."""
     if not groups:
         return
-    _check_groups(groups)
+    dev = _check_groups(groups)
     garr, keep = _groups_c(groups)
     h, tab = hp.to_c()
-    L.check(L.lib().ma_muon_step_noalloc(garr, len(groups), C.byref(h), C.c_void_p(_stream(groups[0].device, stream))))
+    with torch.cuda.device(dev):   # the library's scratch array is the current device's
+        L.check(L.lib().ma_muon_step_noalloc(garr, len(groups), C.byref(h), C.c_void_p(_stream(dev, stream))))
 
 
 def muon_nonfinite(groups: Sequence[MuonGroup], hp: MuonHParams, workspace: torch.Tensor) -> List[bool]:
@@ -355,9 +356,10 @@ def optimizer_step(groups: Sequence[MuonGroup], hp: MuonHParams, adamw_segments:
     garr, keep = _groups_c(groups)
     h, tab = hp.to_c()
     arr, n_seg = _adamw_c(adamw_segments)
-    L.check(L.lib().ma_muon_adamw_step(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
-                                       workspace.numel(), arr, n_seg, int(background_workgroups),
-                                       C.c_void_p(_stream(dev)), C.c_void_p(side.cuda_stream)))
+    with torch.cuda.device(dev):   # the library's fork and join events are the current device's
+        L.check(L.lib().ma_muon_adamw_step(garr, len(groups), C.byref(h), C.c_void_p(workspace.data_ptr()),
+                                           workspace.numel(), arr, n_seg, int(background_workgroups),
+                                           C.c_void_p(_stream(dev)), C.c_void_p(side.cuda_stream)))
     return workspace
 
 

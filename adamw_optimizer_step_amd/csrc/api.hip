@@ -956,6 +956,22 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
+// The library's own per-device objects (the scratch array, the fork and join
+// events) are the current device's: a stream of another device must not be
+// given them.
+int check_stream_device(void* stream, const char* what) {
+  int cur = 0;
+  hipError_t err = hipGetDevice(&cur);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (!stream) return MA_OK;
+  hipDevice_t sd = 0;
+  err = hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sd);
+  if (err != hipSuccess) return hip_fail(err, "hipStreamGetDevice");
+  if ((int)sd != cur)
+    return fail(MA_ERR_INVALID_ARG, "%s belongs to device %d while device %d is current", what, (int)sd, cur);
+  return MA_OK;
+}
+
 // The current device's address of `scratch` (looked up on the device's first
 // call, with that device current).
 int scratch_for_current_device(void** out) {
@@ -987,6 +1003,7 @@ int ma_muon_step_noalloc(const ma_muon_group* groups, int32_t n_groups, const ma
     return fail(MA_ERR_WORKSPACE, "the step needs %zu bytes of scratch; ma_muon_step_noalloc has %zu (use ma_muon_step)",
                 plan.bytes, (size_t)MA_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
+  if ((rc = check_stream_device(stream, "the stream"))) return rc;
   if ((rc = scratch_for_current_device(&ws))) return rc;
   return muon_enqueue(plan, hp, ws, nullptr, stream);
 }
@@ -1178,6 +1195,8 @@ int ma_muon_adamw_step(const ma_muon_group* groups, int32_t n_groups, const ma_m
   if (rc) return rc;
   if ((rc = adamw_prepare(segs, n_segs, rs))) return rc;
   if ((rc = check_overlaps(rs))) return rc;
+  if ((rc = check_stream_device(stream, "stream")) || (rc = check_stream_device(side_stream, "side_stream")))
+    return rc;
   const bool inject = g_fail_after_fork;
   g_fail_after_fork = false;
   hipEvent_t e_fork = nullptr, e_join = nullptr;

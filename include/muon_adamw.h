@@ -192,7 +192,9 @@ int ma_muon_step(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hp
  * from different host threads) race and must be ordered by the caller. Each
  * call writes every byte of scratch it later reads, so nothing carries over
  * from an earlier call. With check_finite, ma_muon_nonfinite is not available
- * for this entry point (the flags live in the shared array). */
+ * for this entry point (the flags live in the shared array). The array used
+ * is the current device's: a stream of another device is rejected with
+ * MA_ERR_INVALID_ARG. */
 #define MA_NOALLOC_SCRATCH_BYTES (64u << 20)
 int ma_muon_step_noalloc(const ma_muon_group* groups, int32_t n_groups, const ma_muon_hparams* hp, void* stream);
 
@@ -290,7 +292,8 @@ int ma_adamw_step_background(const ma_adamw_segment* segments, int32_t n_segment
  * any later work. Results are those of ma_muon_step followed by
  * ma_adamw_step. side_stream must differ from stream (both may be captured
  * into one HIP graph: the fork and join are event records and waits on
- * events the library creates once per device and host thread). Every
+ * events the library creates once per device and host thread; both streams
+ * must belong to the current device, MA_ERR_INVALID_ARG otherwise). Every
  * argument is validated before the first launch, and no two buffers of the
  * two steps (Muon parameters, gradients, momentum, the workspace, AdamW
  * buffers) may overlap (MA_ERR_INVALID_ARG). If a launch fails after the
