@@ -8,7 +8,9 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -33,17 +35,72 @@ FLAGS = [
 LINK = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
 
 
-def _compile(src: str) -> str:
+# Per-kernel register budgets, checked on every build from the compiler's
+# resource-usage remarks. The persistent GEMM runs two waves per SIMD; the
+# AdamW update may run beside it on another stream, and one of its waves must
+# fit in what the two leave of a SIMD's 512 VGPRs per lane (allocated in
+# granules of 8), or a GEMM block cannot start on a CU where an AdamW wave is
+# resident and waits for it to end. No kernel may use scratch memory.
+VGPR_FILE, VGPR_GRANULE = 512, 8
+GEMM_KERNEL, GEMM_WAVES_PER_SIMD = "ns_gemm_dma", 2
+BESIDE_KERNEL = "k_adamw_lean"
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|LDS Size \[bytes/block\]):\s+(\S+)")
+
+
+def _alloc(n: int) -> int:
+    return -(-max(n, 1) // VGPR_GRANULE) * VGPR_GRANULE
+
+
+def parse_resources(text: str) -> dict:
+    """{kernel: {"vgprs", "agprs", "scratch", "lds"}} from the text of
+    ``-Rpass-analysis=kernel-resource-usage`` remarks."""
+    out, cur = {}, None
+    keys = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch", "LDS Size [bytes/block]": "lds"}
+    for m in _REMARK.finditer(text):
+        if m.group(1) == "Function Name":
+            cur = out.setdefault(m.group(2), {})
+        elif cur is not None:
+            cur[keys[m.group(1)]] = int(m.group(2))
+    return out
+
+
+def check_resources(res: dict) -> list:
+    """The budget violations in ``res`` (see parse_resources), as messages."""
+    bad = [f"{k}: {v['scratch']} bytes of scratch per lane" for k, v in res.items() if v.get("scratch", 0)]
+    beside = [v["vgprs"] + v.get("agprs", 0) for k, v in res.items() if BESIDE_KERNEL in k]
+    if beside:
+        room = VGPR_FILE - _alloc(max(beside))
+        for k, v in res.items():
+            if GEMM_KERNEL in k and GEMM_WAVES_PER_SIMD * _alloc(v["vgprs"] + v.get("agprs", 0)) > room:
+                bad.append(f"{k}: {v['vgprs'] + v.get('agprs', 0)} VGPRs; {GEMM_WAVES_PER_SIMD} waves leave no room "
+                           f"for a wave of {BESIDE_KERNEL} ({max(beside)})")
+    return bad
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    lines = (r.stderr or "").splitlines()
+    res = parse_resources("\n".join(lines))
+    # the remarks, each with its source excerpt, are not echoed
+    err, skip = [], 0
+    for l in lines:
+        if "kernel-resource-usage" in l:
+            skip = 2 if "Function Name" in l else 0
+            continue
+        if skip:
+            skip -= 1
+            continue
+        if noise not in l:
+            err.append(l)
+    err = "\n".join(err)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
     if err.strip():
         print(err, file=sys.stderr)
-    return obj
+    return obj, res
 
 
 # Host-side sanitizers for the planner and argument validation (api.hip, the
@@ -76,7 +133,7 @@ def build_host_sanitized(verbose: bool = True) -> str:
             obj = os.path.join(BUILD, os.path.basename(src) + ".o")
             fresh = os.path.exists(obj) and os.path.getmtime(obj) >= max(
                 os.path.getmtime(f) for f in glob.glob(os.path.join(CSRC, "*")))
-            objs.append(obj if fresh else _compile(src))
+            objs.append(obj if fresh else _compile(src)[0])
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", SAN_LIB],
                        capture_output=True, text=True)
     if r.returncode != 0:
@@ -97,7 +154,14 @@ def build(verbose: bool = True) -> str:
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = min(len(sources), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, sources))
+        done = list(ex.map(_compile, sources))
+    objs = [o for o, _ in done]
+    res = {k: v for _, r in done for k, v in r.items()}
+    with open(os.path.join(BUILD, "resources.json"), "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    bad = check_resources(res)
+    if bad:
+        raise RuntimeError("kernel resource budget exceeded:\n  " + "\n  ".join(bad))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

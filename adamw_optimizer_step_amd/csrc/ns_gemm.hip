@@ -33,6 +33,8 @@
 // shape group, whole matrices at a time where possible (see NsArgs).
 #include "ns_gemm.hpp"
 
+#include <type_traits>
+
 namespace ma {
 
 template <int DT> struct MfmaTraits;
@@ -569,8 +571,13 @@ constexpr int RPI = 1024 / ROWB;                  // rows per 1 KiB DMA instruct
 constexpr int KK = BK / 16;                       // MFMA k-steps per k-tile
 constexpr int STAGE_BYTES = (BM + BN) * ROWB;     // P rows 0..255, Q rows 256..511
 constexpr int MAIN = STAGES * STAGE_BYTES;
-constexpr int EPI = EpiSmem<DT_BF16, BM, BN>::BYTES;
-constexpr int BYTES = MAIN > EPI ? MAIN : EPI;
+// The epilogue stages each wave's output block through a private area of 64
+// rows of LDW values above stage 0 (which may already hold the block's next
+// job's first k-tile); rows stay 16-byte aligned
+constexpr int LDW = 64 + MfmaTraits<DT_BF16>::kPad;
+constexpr int EPI_WAVE = 64 * LDW * 2;
+constexpr int EPI_END = STAGE_BYTES + 8 * EPI_WAVE;
+constexpr int BYTES = MAIN > EPI_END ? MAIN : EPI_END;
 static_assert(BK == 64 && KK == 4, "k-tiles of 64: four MFMA k-steps");
 static_assert(STAGES >= 2 && BYTES <= 160 * 1024, "LDS ring must fit in 160 KiB");
 // per wave-grid sizes: wave sub-tile WTM x WTN of FM x FN 32x32 blocks; each
@@ -599,6 +606,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 #define MA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// Block barrier for LDS: this wave's LDS accesses are complete, then
+// s_barrier. Unlike __syncthreads it does not wait for outstanding global
+// loads and stores, so LDS-DMA fills and output stores stay in flight across
+// it (a DMA's own landing is waited for with dma_wait_tiles); the memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // wait until at most `tiles` k-tile DMAs of this wave are outstanding
 template <int DPW>
@@ -794,6 +808,12 @@ struct DmaCtx {
   int lane_off_t[2];
   uint32_t poff[4];
   float a;
+  // the block's next job, whose k-tile 0 this wave loads into stage 0 after
+  // its last k-tile (pre): its source, as src / q_step / lane_off
+  bool pre;
+  const uint16_t* n_src;
+  int64_t n_q_step;
+  int n_lane_off[2];
 };
 
 // k-step KKI of k-tile kt: its MFMAs run on the fragments in (fa, fb) while
@@ -915,12 +935,6 @@ __device__ __forceinline__ void dma_ktile(const DmaCtx& c, int kt,
   dma_kstep<3, IIB, WGM, WGN, QT, PT>(c, kt, acc, f1a, f1b, f0a, f0b);
 }
 
-// One output tile: prologue DMA, main loop, epilogue.
-// FOLD: the term that is not a product of the two operands -- a X in AXPY,
-// b A in POLY (as (b/c) A, the epilogue then scaling by c; needs c != 0) --
-// is added inside the main loop by scaled-identity MFMAs against the Q
-// fragments, so the epilogue reads nothing back from global memory. AXPY
-// always folds.
 // Job slot in LDS: the block's next job (gi, mat, bi, bj; gi < 0: none),
 // written by wave 0 while its first operand DMA is in flight
 __device__ __forceinline__ void put_job(int* slot, bool ok, const TileJob& N) {
@@ -930,24 +944,15 @@ __device__ __forceinline__ void put_job(int* slot, bool ok, const TileJob& N) {
   slot[3] = N.bj;
 }
 
-// next_slot (optional): where wave 0 stores job `next_local` of XCD `xcd`'s
-// list, so that the other waves need not map it
-template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD>
-__device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem,
-                                         int xcd = 0, int next_local = 0, int* next_slot = nullptr) {
+// This wave's DMA context for job J: operand sources, fragment addresses and
+// the transposed-read bounds (the pipeline state apart from the accumulators)
+template <int EPI, int WGM, int WGN, bool QT>
+__device__ __forceinline__ DmaCtx dma_ctx(const NsArgs& args, const TileJob& J, unsigned char* smem, int wave,
+                                          int lane) {
   using namespace dma;
   using Gd = Grid<WGM, WGN>;
-  constexpr int FM = Gd::FM, FN = Gd::FN, DPW = Gd::DPW, NW = Gd::NW;
+  constexpr int DPW = Gd::DPW, NW = Gd::NW;
   const NsGroup& G = args.g[J.gi];
-  // an opaque copy of the thread index: without it the compiler hoists every
-  // lane-dependent address of the tile out of a persistent block's job loop
-  // and keeps them all live, through the epilogue too
-  int opaque;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(opaque) : "v"((int)threadIdx.x));
-  const int lane = opaque & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int tid = (wave << 6) | lane;
-
   // DMA source of this wave: the first NW/2 waves load P rows
   // [w*PANEL, +PANEL), the others the matching rows of Q; P and Q rows are
   // contiguous in the stage.
@@ -957,7 +962,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   c.lane = lane;
   c.wm = wave / WGN;
   c.wn = wave % WGN;
-  c.nk = G.K / BK;   // K is a multiple of 256: nk >= 4
+  c.nk = G.K / BK;   // K is a multiple of 256: nk >= 4, a multiple of 4
   c.a = EPI == EPI_POLY ? args.b / args.c : args.a;
   const bool isP = wave < NW / 2;
   c.ld_src = isP ? G.ldP : G.ldQ;
@@ -1017,6 +1022,294 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
       }
     }
   }
+  c.pre = false;
+  return c;
+}
+
+// The source of this wave's share of job J's tile 0 (dma_ctx's src / q_step /
+// lane_off, or its transposed *_t form for a P wave of a QT job with bi > 0),
+// as the next job's source of a DmaCtx
+template <int WGM, int WGN, bool QT>
+__device__ __forceinline__ void dma_next_src(const NsArgs& args, const TileJob& J, int wave, int lane, DmaCtx& c) {
+  using namespace dma;
+  using Gd = Grid<WGM, WGN>;
+  constexpr int NW = Gd::NW;
+  const NsGroup& G = args.g[J.gi];
+  const bool isP = wave < NW / 2;
+  const int ld = isP ? G.ldP : G.ldQ;
+  c.pre = true;
+  if (QT && (!isP || (G.p_upper && J.bi > 0))) {
+    // rows k 0..63 of Q^T (Q waves) or of B's stored upper triangle (P waves
+    // left of the diagonal block), two 512-byte rows per instruction
+    const uint16_t* base = isP ? reinterpret_cast<const uint16_t*>(G.P) + (int64_t)J.mat * G.sP +
+                                     (int64_t)(wave * 16) * ld + (int64_t)J.bi * BM
+                               : reinterpret_cast<const uint16_t*>(G.Q) + (int64_t)J.mat * G.sQ +
+                                     (int64_t)((wave - NW / 2) * 16) * ld + (int64_t)J.bj * BN;
+    c.n_src = base;
+    c.n_q_step = 2 * (int64_t)ld;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      c.n_lane_off[par] = (lane >> 5) * ld + (((lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3))) << 3);
+  } else {
+    c.n_src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
+              (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave % (NW / 2)) * Gd::PANEL) * ld;
+    c.n_q_step = (int64_t)RPI * ld;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      c.n_lane_off[par] = (lane / CPR) * ld + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
+  }
+}
+
+// f(std::integral_constant<int, I>()) for I = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
+// the LDS byte address of a pointer into a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const unsigned char lds_cu8_t;
+  return (uint32_t)(uintptr_t)(lds_cu8_t*)p;
+}
+
+// LDS accesses of the epilogue staging in asm: before a compiler-visible LDS
+// access that it cannot tell apart from the target of an LDS-DMA load in
+// flight, the compiler waits for every vector-memory operation, and the
+// staging lies above stage 0, where the next job's tile 0 is landing.
+// One 8-byte staging write at byte address addr + OFF.
+template <int OFF>
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, uint32_t lo, uint32_t hi) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = {lo, hi};
+  asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+// Four 16-byte reads at byte addresses addr + u * STEP (u = 0..3), waited
+// for inside the statement
+template <int STEP>
+__device__ __forceinline__ void lds_read4_b128(uint32_t addr, u32x4_t (&v)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:%5\n\t"
+      "ds_read_b128 %2, %4 offset:%6\n\t"
+      "ds_read_b128 %3, %4 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(addr), "i"(STEP), "i"(2 * STEP), "i"(3 * STEP)
+      : "memory");
+}
+
+// Epilogue of the LDS-DMA kernel (accumulators transposed, bf16 output): the
+// a/b/c combination of ns_epilogue, then each wave writes out its own 128 x 64
+// block through its private staging area above stage 0, 64 output rows at a
+// time and with no block barrier: it reads back only what it staged, 16
+// bytes per lane, so that each store instruction writes eight whole 128-byte
+// rows. Stage 0, where the next job's tile 0 may be landing, is not touched.
+// S_N (rows i, contiguous j) stages the block itself, S_T (rows j, contiguous
+// i) its transpose, for the mirror tile of a symmetric product.
+// mirror: a diagonal tile of a symmetric product, whose waves below the
+// diagonal (rows 128..255, columns 0..127; skip: this wave is one) ran no
+// MFMAs; those rows are the transpose of rows 0..127, columns 128..255, which
+// waves (0, 2) and (0, 3) also write out transposed (the tile comes out
+// exactly symmetric). sc: the operand scale (GRAM, AXPY; 1 without one),
+// loaded before the main loop.
+template <int EPI, int WGM, int WGN, bool E_DONE, bool UPD>
+__device__ __forceinline__ void dma_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
+                                             f32x16_t (&acc)[dma::Grid<WGM, WGN>::FM][dma::Grid<WGM, WGN>::FN],
+                                             unsigned char* smem, int tid, bool mirror, bool skip, float sc) {
+  using namespace dma;
+  using Gd = Grid<WGM, WGN>;
+  using T = uint16_t;
+  static_assert(!UPD || EPI == EPI_AXPY, "the update is fused into the AXPY only");
+  constexpr int WTM = Gd::WTM, WTN = Gd::WTN, FM = Gd::FM, FN = Gd::FN, VEC = 8;
+  static_assert(WGM == 2 && WGN == 4 && WTM == 128 && WTN == 64 && FM == 4 && FN == 2, "waves of 128 x 64");
+  // an opaque copy of the thread index: the lane-dependent addresses below
+  // are then computed here, not kept in registers through the main loop
+  int opaque;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(opaque) : "v"(tid));
+  const int lane = opaque & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int mat = J.mat, bi = J.bi, bj = J.bj;
+  const bool diag = G.symmetric && bi == bj;
+  // a symmetric product writes its tile (bi, bj) and the mirror (bj, bi), the
+  // diagonal tiles once; upper_only drops the mirrors
+  T* outT = (diag || (G.symmetric && G.upper_only)) ? nullptr : reinterpret_cast<T*>(G.outT);
+  T* outN = reinterpret_cast<T*>(G.outN);
+
+  if constexpr (EPI != EPI_GRAM && !E_DONE) {
+    // E[i][j..j+3] (= E[j][i..], E = A symmetric): one 32x32 block at a time
+    static_assert(EPI == EPI_POLY, "transposed accumulators read E as a symmetric matrix");
+    const T* Eg = reinterpret_cast<const T*>(G.E) + (int64_t)mat * G.sE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float e[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int il = wm * WTM + i * 32 + l32, jl = wn * WTN + j * 32 + q * 8 + lh * 4;
+          const uint2 u = *reinterpret_cast<const uint2*>(Eg + (int64_t)(bi * BM + il) * G.ldE + bj * BN + jl);
+          e[q][0] = __uint_as_float(u.x << 16); e[q][1] = __uint_as_float(u.x & 0xFFFF0000u);
+          e[q][2] = __uint_as_float(u.y << 16); e[q][3] = __uint_as_float(u.y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][4 * q + r] = __builtin_fmaf(args.b, e[q][r], args.c * acc[i][j][4 * q + r]);
+        asm volatile("" ::: "memory");
+      }
+  }
+  if constexpr (EPI != EPI_POLY) {
+    // X = s Y with Y in the operand buffers: A = s^2 Y Y^T, X' = s (a Y + B Y)
+    if (G.scale) {
+      const float s2 = EPI == EPI_GRAM ? sc * sc : sc;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= s2;
+    }
+  }
+  if constexpr (EPI == EPI_POLY && E_DONE) {
+    // the main loop accumulated A A + (b/c) A
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] *= args.c;
+  }
+
+  // this wave's staging area; lane reads back row rr + 8u (u = 0..7), values
+  // rc .. rc+7
+  T* const wst = reinterpret_cast<T*>(smem + STAGE_BYTES + wave * EPI_WAVE);
+  const int rr = lane >> 3, rc = (lane & 7) * VEC;
+  const uint32_t rd = lds_addr(wst + rr * LDW + rc);
+  // the block's first output row and column
+  const int i0 = bi * BM + wm * WTM, j0 = bj * BN + wn * WTN;
+  // The block transposed, half h (block rows h*64 .. +63) at a time: staging
+  // row = block column (64), contiguous block rows; stored to rows j0 + 0..63,
+  // columns i0 + h*64 .. of the matrix at dst (pitch ld).
+  auto store_t = [&](T* dst, int64_t ld, bool upd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            stage4_strided<DT_BF16>(wst + (j * 32 + q * 8 + lh * 4) * LDW + ii * 32 + l32, LDW, acc[2 * h + ii][j], q);
+      uint4 wc[UPD ? 8 : 1];
+      if constexpr (UPD) {
+        if (upd) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) wload(G, mat, j0 + rr + 8 * u, i0 + h * 64 + rc, wc[u]);
+        }
+      }
+      // the weight chunks have landed: one wait here (on every path, so that
+      // the compiler knows it), rather than the compiler's wait for
+      // everything in flight before each use (the LDS-DMA load in flight
+      // makes it count vector-memory operations as unordered)
+      if constexpr (UPD) MA_WAIT_VMCNT(0);
+      u32x4_t sv[4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u % 4 == 0) lds_read4_b128<8 * LDW * 2>(rd + (u / 4) * (32 * LDW * 2), sv);
+        const uint4 v = make_uint4(sv[u % 4][0], sv[u % 4][1], sv[u % 4][2], sv[u % 4][3]);
+        *reinterpret_cast<uint4*>(dst + (int64_t)(rr + 8 * u) * ld + h * 64 + rc) = v;
+        if constexpr (UPD)
+          if (upd) wapply(G, mat, j0 + rr + 8 * u, i0 + h * 64 + rc, wc[u], v);
+      }
+    }
+  };
+
+  if (outT) {
+    const bool upd = UPD && G.W && G.w_trans && !(G.nonfinite && G.nonfinite[mat]);
+    store_t(outT + (int64_t)mat * G.sT + (int64_t)j0 * G.ldT + i0, G.ldT, upd);
+  }
+  if (outN && !skip) {
+    // the block row-major, half h (block rows h*64 .. +63) at a time: lane
+    // (l32, lh) stages block row h*64 + ii*32 + l32 at staging row ii*32 + l32,
+    // columns j*32 + q*8 + lh*4 .. +3
+    T* const dst = outN + (int64_t)mat * G.sN + (int64_t)i0 * G.ldN + j0;
+    const bool upd = UPD && G.W && !G.w_trans && !(G.nonfinite && G.nonfinite[mat]);
+    const uint32_t wr = lds_addr(wst + l32 * LDW + lh * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      static_for<0, 2 * FN * 4>([&](auto k) {
+        constexpr int ii = decltype(k)::value / (FN * 4), j = decltype(k)::value / 4 % FN, q = decltype(k)::value % 4;
+        const f32x16_t& a = acc[2 * h + ii][j];
+        lds_write_b64<(ii * 32 * LDW + j * 32 + q * 8) * 2>(wr, pack_bf16x2(a[4 * q], a[4 * q + 1]),
+                                                            pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+      });
+      uint4 wc[UPD ? 8 : 1];
+      if constexpr (UPD) {
+        if (upd) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) wload(G, mat, i0 + h * 64 + rr + 8 * u, j0 + rc, wc[u]);
+        }
+      }
+      if constexpr (UPD) MA_WAIT_VMCNT(0);   // the weight chunks have landed (as above)
+      u32x4_t sv[4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u % 4 == 0) lds_read4_b128<8 * LDW * 2>(rd + (u / 4) * (32 * LDW * 2), sv);
+        const int row = h * 64 + rr + 8 * u;
+        const uint4 v = make_uint4(sv[u % 4][0], sv[u % 4][1], sv[u % 4][2], sv[u % 4][3]);
+        *reinterpret_cast<uint4*>(dst + (int64_t)row * G.ldN + rc) = v;
+        if constexpr (UPD)
+          if (upd) wapply(G, mat, i0 + row, j0 + rc, wc[u], v);
+      }
+    }
+  }
+  // the mirror: output rows j0 + 0..63 (below the diagonal), columns i0 ..
+  if (mirror && wm == 0 && wn * WTN >= BN / 2) store_t(outN + (int64_t)mat * G.sN + (int64_t)j0 * G.ldN + i0, G.ldN, false);
+}
+
+// One output tile: prologue DMA, main loop, epilogue.
+// FOLD: the term that is not a product of the two operands -- a X in AXPY,
+// b A in POLY (as (b/c) A, the epilogue then scaling by c; needs c != 0) --
+// is added inside the main loop by scaled-identity MFMAs against the Q
+// fragments, so the epilogue reads nothing back from global memory. AXPY
+// always folds.
+// Wave 0 stores job `next_local` of XCD `xcd`'s list in next_slot while the
+// first k-tiles land; every wave reads it after the prologue barrier (next,
+// have_next).
+// PRE (the AXPY, whose first k-tile otherwise waits behind the previous
+// tile's output stores): each wave loads its share of the next job's tile 0
+// into stage 0 (free since the barrier after tile nk - 2) once its last
+// k-step's MFMAs are issued (DmaCtx::pre), so that its latency overlaps
+// their drain and the epilogue, which stages in halves above stage 0;
+// pre_issued: this job's tile 0 was loaded so. In GRAM and POLY the extra
+// staging barriers cost more than the shorter first wait saves.
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD, bool PRE>
+__device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem, int xcd,
+                                         int next_local, int* next_slot, bool pre_issued, TileJob& next,
+                                         bool& have_next) {
+  using namespace dma;
+  using Gd = Grid<WGM, WGN>;
+  constexpr int FM = Gd::FM, FN = Gd::FN, DPW = Gd::DPW;
+  const NsGroup& G = args.g[J.gi];
+  // an opaque copy of the thread index: without it the compiler hoists every
+  // lane-dependent address of the tile out of a persistent block's job loop
+  // and keeps them all live, through the epilogue too
+  int opaque;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(opaque) : "v"((int)threadIdx.x));
+  const int lane = opaque & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int tid = (wave << 6) | lane;
+  DmaCtx c = dma_ctx<EPI, WGM, WGN, QT>(args, J, smem, wave, lane);
+  // the operand scale (written by an earlier launch), read through the
+  // constant address space: a scalar load, which no wait for the DMA in
+  // flight holds up
+  typedef __attribute__((address_space(4))) const float const_f32_t;
+  const float sc = (EPI != EPI_POLY && G.scale) ? *((const_f32_t*)G.scale + (int64_t)J.mat * G.scale_stride) : 1.0f;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -1032,27 +1325,41 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   // run.
 #pragma unroll
   for (int t = 0; t < STAGES; ++t) {
+    if (PRE && t == 0 && pre_issued) continue;
     if (QT && t < c.dma_t_end)
       dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src_t, c.q_step_t, c.lane_off_t, (int64_t)t * c.k_step_t);
     else
       dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src, c.q_step, c.lane_off, (int64_t)t * c.k_step);
   }
-  if (next_slot && wave == 0) {
+  if (wave == 0) {
     // the next job's (scalar) mapping, while the first k-tiles land
     TileJob N;
     const bool ok = map_job_at(args, xcd, next_local, N);
     if (lane == 0) put_job(next_slot, ok, N);
   }
-  dma_wait_tiles<DPW>(STAGES - 1);   // this wave's part of tile 0 has landed
-  __builtin_amdgcn_s_barrier();
+  // this wave's part of tile 0 has landed (tile 0 was issued before tile 1,
+  // here or during the previous job: loads land in order), and the slot is
+  // written
+  dma_wait_tiles<DPW>(STAGES - 1);
+  lds_barrier();
+  next.gi = __builtin_amdgcn_readfirstlane(next_slot[0]);
+  next.mat = __builtin_amdgcn_readfirstlane(next_slot[1]);
+  next.bi = __builtin_amdgcn_readfirstlane(next_slot[2]);
+  next.bj = __builtin_amdgcn_readfirstlane(next_slot[3]);
+  have_next = next.gi >= 0;
+  c.n_src = c.src;
+  c.n_q_step = c.q_step;
+  c.n_lane_off[0] = c.lane_off[0];
+  c.n_lane_off[1] = c.lane_off[1];
+  if (PRE && have_next) dma_next_src<WGM, WGN, QT>(args, next, wave, lane, c);
   // a diagonal tile of a symmetric product: the waves whose blocks all lie
   // below the diagonal (rows 128..255, columns 0..127) compute nothing
   const bool mirror_lower = !QT && G.symmetric && J.bi == J.bj;
   if (mirror_lower && c.wm * Gd::WTM >= BM / 2 && (c.wn + 1) * Gd::WTN <= BN / 2) {
     static_assert(QT || BM == BN, "square tiles");
     dma_skip_ktiles<WGM, WGN>(c);
-    __syncthreads();
-    ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true, UPD>(args, G, J, acc, smem, tid, true);
+    if (PRE && c.pre) dma_issue<DPW>(c.wave_fill, c.n_src, c.n_q_step, c.n_lane_off, 0);
+    lds_barrier();   // as the other waves' barrier before their epilogue
     return;
   }
   u32x4_t f0a[FM], f0b[FN], f1a[FM], f1b[FN];
@@ -1080,8 +1387,11 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
     dma_ktile<2, WGM, WGN, QT>(c, kt++, acc, f0a, f0b, f1a, f1b);
   }
   for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
-  __syncthreads();   // operand tiles no longer needed; LDS is reused below
-  ns_epilogue<DT_BF16, EPI, BM, BN, WGM, WGN, FOLD, true, UPD>(args, G, J, acc, smem, tid, mirror_lower);
+  // stage 0 last held tile nk - 2 (nk is a multiple of 4), which every wave
+  // had read before the barrier at the end of that tile
+  if (PRE && c.pre) dma_issue<DPW>(c.wave_fill, c.n_src, c.n_q_step, c.n_lane_off, 0);
+  lds_barrier();   // every wave has read the last k-tile (stage 1, reused by the staging)
+  dma_epilogue<EPI, WGM, WGN, FOLD, UPD>(args, G, J, acc, smem, tid, mirror_lower, false, sc);
 }
 
 // Persistent over its XCD's job list: block b (XCD b % 8, P blocks per XCD)
@@ -1105,21 +1415,25 @@ ns_gemm_dma(const NsArgs args) {
   __builtin_amdgcn_s_setprio(1);
   const int x = (int)(blockIdx.x & 7);
   const int P = (int)(gridDim.x >> 3);
+  constexpr bool PRE = QT;
   TileJob J;
   int local = (int)(blockIdx.x >> 3);
   bool have = map_job_at(args, x, local, J);
+  bool pre = false;
   // job j's successor goes to slot (j + 1) & 1: a slot is rewritten two jobs
-  // later, after every wave has passed the barrier that follows its reads
+  // later, after every wave has passed the barriers that follow its reads
   for (int j = 0; have; ++j) {
     int* const slot = slots + 4 * ((j + 1) & 1);
-    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD>(args, J, smem, x, local + P, slot);
-    __syncthreads();   // the epilogue is done with LDS before the next job's DMA
+    TileJob N;
+    bool more;
+    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD, PRE>(args, J, smem, x, local + P, slot, pre, N, more);
+    // every wave has read the staged output before the next job's DMA lands
+    // over it (with PRE its tile 0, in stage 0, is already in flight)
+    lds_barrier();
     local += P;
-    have = slot[0] >= 0;
-    J.gi = slot[0];
-    J.mat = slot[1];
-    J.bi = slot[2];
-    J.bj = slot[3];
+    J = N;
+    have = more;
+    pre = PRE && more;
   }
 }
 
