@@ -150,12 +150,11 @@ __device__ __forceinline__ void stage4_strided(typename MfmaTraits<DT>::T* p, in
   }
 }
 
-// The fused update (see NsGroup::W; bf16 weights): the weight chunks a thread
-// updates are loaded before the tile's U is read back from LDS (wload), so
-// that their latency overlaps the staging barrier and the U stores; each
-// 8-value chunk at parameter row pr, columns pc .. pc+7 of matrix `mat` is
-// then updated with muon_update and written back (wapply). Both accesses
-// non-temporal.
+// The fused update (see NsGroup::W; bf16 weights): the weight chunks a lane
+// updates are loaded before its wave reads the staged U back from LDS
+// (wload), so that their latency overlaps the read-back; each 8-value chunk
+// at parameter row pr, columns pc .. pc+7 of matrix `mat` is then updated
+// with muon_update and written back (wapply). Both accesses non-temporal.
 __device__ __forceinline__ bool w_in(const NsGroup& G, int pr, int pc) { return pr < G.R && pc < G.C; }
 __device__ __forceinline__ void wload(const NsGroup& G, int mat, int pr, int pc, uint4& w) {
   if (!w_in(G, pr, pc)) return;   // padding of the iteration buffers
@@ -185,51 +184,40 @@ struct EpiSmem {
   static constexpr int BYTES = (BN * LDT > BM * LDN ? BN * LDT : BM * LDN) * Tr::kElem;
 };
 
-// Accumulator layout of a 32x32 MFMA block: lane l holds column (l % 32) and,
-// in registers 4q..4q+3, rows 8q + 4(l/32) + 0..3. ACC_T: the block was
-// accumulated transposed (operands swapped in the MFMA), so lane l holds row
-// (l % 32) and columns 8q + 4(l/32) + 0..3; row-major staging then writes 8
-// bytes per lane, the transposed staging 2. The caller has finished with LDS
-// (a barrier precedes the call).
-template <int DT, int EPI, int BM, int BN, int WGM, int WGN, bool E_DONE = false, bool ACC_T = false,
-          bool UPD = false>
+// Epilogue of the register-staged kernel. Accumulator layout of a 32x32 MFMA
+// block: lane l holds column (l % 32) and, in registers 4q..4q+3, rows
+// 8q + 4(l/32) + 0..3; the transposed staging then writes 8 bytes per lane,
+// the row-major one 2. The caller has finished with LDS (a barrier precedes
+// the call).
+template <int DT, int EPI, int BM, int BN, int WGM, int WGN>
 __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G, const TileJob& J,
-                                            f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
-                                            unsigned char* smem, int tid_in = -1, bool mirror_lower = false) {
+                                            f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32], unsigned char* smem) {
   using Tr = MfmaTraits<DT>;
   using T = typename Tr::T;
   using ES = EpiSmem<DT, BM, BN>;
-  static_assert(!UPD || (EPI == EPI_AXPY && DT == DT_BF16), "the update is fused into the bf16 AXPY only");
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int VEC = 16 / Tr::kElem;
-  const int tid = tid_in >= 0 ? tid_in : (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, lh = lane >> 5;
   const int mat = J.mat, bi = J.bi, bj = J.bj;
   const bool diag = G.symmetric && bi == bj;
   // a symmetric product writes its tile (bi, bj) and the mirror (bj, bi),
-  // the diagonal tiles once (in the layout whose staging is cheaper: the
-  // two are the same block, of the same buffer); upper_only drops the mirrors
-  T* outT = ((ACC_T && diag) || (G.symmetric && G.upper_only && !diag)) ? nullptr : reinterpret_cast<T*>(G.outT);
-  T* outN = (!ACC_T && diag) ? nullptr : reinterpret_cast<T*>(G.outN);
+  // the diagonal tiles once (transposed: the cheaper staging; the two are the
+  // same block of the same buffer); upper_only drops the mirrors
+  T* outT = (G.symmetric && G.upper_only && !diag) ? nullptr : reinterpret_cast<T*>(G.outT);
+  T* outN = diag ? nullptr : reinterpret_cast<T*>(G.outN);
   // (il, jl): the output row and column of register 4q of block (i, j)
   auto rc = [&](int i, int j, int q, int& il, int& jl) __attribute__((always_inline)) {
-    if constexpr (ACC_T) {
-      il = wm * WTM + i * 32 + l32;
-      jl = wn * WTN + j * 32 + q * 8 + lh * 4;
-    } else {
-      il = wm * WTM + i * 32 + q * 8 + lh * 4;
-      jl = wn * WTN + j * 32 + l32;
-    }
+    il = wm * WTM + i * 32 + q * 8 + lh * 4;
+    jl = wn * WTN + j * 32 + l32;
   };
 
-  if constexpr (EPI != EPI_GRAM && !E_DONE) {
+  if constexpr (EPI != EPI_GRAM) {
     // E[j][i..i+3]: A (symmetric) for POLY, X^T for AXPY; one 32x32 block at
     // a time, so that the loads of all blocks are not held in registers at once.
-    // ACC_T reads E[i][j..j+3], which is the same value only for symmetric A.
-    static_assert(!ACC_T || EPI == EPI_POLY, "transposed accumulators read E as a symmetric matrix");
     const T* Eg = reinterpret_cast<const T*>(G.E) + (int64_t)mat * G.sE;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -240,8 +228,7 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
         for (int q = 0; q < 4; ++q) {
           int il, jl;
           rc(i, j, q, il, jl);
-          const T* ep = ACC_T ? Eg + (int64_t)(bi * BM + il) * G.ldE + bj * BN + jl
-                              : Eg + (int64_t)(bj * BN + jl) * G.ldE + bi * BM + il;
+          const T* ep = Eg + (int64_t)(bj * BN + jl) * G.ldE + bi * BM + il;
           if constexpr (DT == DT_BF16) {
             const uint2 u = *reinterpret_cast<const uint2*>(ep);
             e[q][0] = __uint_as_float(u.x << 16); e[q][1] = __uint_as_float(u.x & 0xFFFF0000u);
@@ -276,15 +263,6 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
           for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
     }
   }
-  if constexpr (EPI == EPI_POLY && E_DONE) {
-    // the main loop accumulated A A + (b/c) A
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] *= args.c;
-  }
 
   T* stg = reinterpret_cast<T*>(smem);
   if (outT) {
@@ -297,9 +275,7 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
         for (int q = 0; q < 4; ++q) {
           int il, jl;
           rc(i, j, q, il, jl);
-          if constexpr (ACC_T) {
-            stage4_strided<DT>(stg + jl * ES::LDT + il, ES::LDT, acc[i][j], q);
-          } else if constexpr (DT == DT_BF16) {
+          if constexpr (DT == DT_BF16) {
             uint2 u;
             u.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
             u.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
@@ -312,26 +288,12 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
       }
     T* dst = outT + (int64_t)mat * G.sT + (int64_t)(bj * BN) * G.ldT + bi * BM;
     constexpr int CPR = BM / VEC;   // 16-byte chunks per staged row
-    constexpr int NU = BN * CPR / NT;
-    const bool upd = UPD && G.W && G.w_trans && !(G.nonfinite && G.nonfinite[mat]);
-    uint4 wc[UPD ? NU : 1];
-    if constexpr (UPD) {
-      if (upd) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
-          wload(G, mat, bj * BN + r, bi * BM + ch * VEC, wc[u]);
-        }
-      }
-    }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
+    for (int u = 0; u < BN * CPR / NT; ++u) {
       const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * ES::LDT + ch * VEC);
-      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldT + ch * VEC) = v;
-      if constexpr (UPD)
-        if (upd) wapply(G, mat, bj * BN + r, bi * BM + ch * VEC, wc[u], v);
+      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldT + ch * VEC) =
+          *reinterpret_cast<const uint4*>(stg + r * ES::LDT + ch * VEC);
     }
     if (outN) __syncthreads();
   }
@@ -345,63 +307,17 @@ __device__ __forceinline__ void ns_epilogue(const NsArgs& args, const NsGroup& G
         for (int q = 0; q < 4; ++q) {
           int il, jl;
           rc(i, j, q, il, jl);
-          if constexpr (!ACC_T) {
-            stage4_strided<DT>(stg + il * ES::LDN + jl, ES::LDN, acc[i][j], q);
-          } else if constexpr (DT == DT_BF16) {
-            uint2 u;
-            u.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            u.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *reinterpret_cast<uint2*>(stg + il * ES::LDN + jl) = u;
-          } else {
-            *reinterpret_cast<float4*>(stg + il * ES::LDN + jl) =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          }
+          stage4_strided<DT>(stg + il * ES::LDN + jl, ES::LDN, acc[i][j], q);
         }
       }
-    if constexpr (ACC_T && BM == BN && DT == DT_BF16) {
-      if (mirror_lower && diag) {
-        // rows BM/2.., columns ..BN/2 were not computed (their waves skipped
-        // the K loop): they are the transpose of rows ..BM/2, columns BN/2..
-        // (computed, they would hold the same products, equal to these up to
-        // fp32 rounding: in POLY the folded term enters the two quadrants'
-        // sums at different k-tiles; the mirror makes the diagonal tile
-        // exactly symmetric). Each thread
-        // moves 8 values: one 16-byte read along a row above the diagonal, 8
-        // two-byte writes down a column below it.
-        __syncthreads();
-        constexpr int H = BM / 2, CH = H / 8;
-#pragma unroll
-        for (int u = 0; u < H * CH / NT; ++u) {
-          const int idx = tid + NT * u, cc = idx % H, rc = idx / H;
-          const uint4 v = *reinterpret_cast<const uint4*>(stg + cc * ES::LDN + H + rc * 8);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) stg[(H + rc * 8 + e) * ES::LDN + cc] = (T)(w[e >> 1] >> (16 * (e & 1)));
-        }
-      }
-    }
     T* dst = outN + (int64_t)mat * G.sN + (int64_t)(bi * BM) * G.ldN + bj * BN;
     constexpr int CPR = BN / VEC;
-    constexpr int NU = BM * CPR / NT;
-    const bool upd = UPD && G.W && !G.w_trans && !(G.nonfinite && G.nonfinite[mat]);
-    uint4 wc[UPD ? NU : 1];
-    if constexpr (UPD) {
-      if (upd) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
-          wload(G, mat, bi * BM + r, bj * BN + ch * VEC, wc[u]);
-        }
-      }
-    }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
+    for (int u = 0; u < BM * CPR / NT; ++u) {
       const int idx = tid + NT * u, r = idx / CPR, ch = idx % CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * ES::LDN + ch * VEC);
-      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldN + ch * VEC) = v;
-      if constexpr (UPD)
-        if (upd) wapply(G, mat, bi * BM + r, bj * BN + ch * VEC, wc[u], v);
+      *reinterpret_cast<uint4*>(dst + (int64_t)r * G.ldN + ch * VEC) =
+          *reinterpret_cast<const uint4*>(stg + r * ES::LDN + ch * VEC);
     }
   }
 }
@@ -1281,13 +1197,11 @@ __device__ __forceinline__ void dma_epilogue(const NsArgs& args, const NsGroup& 
 // Wave 0 stores job `next_local` of XCD `xcd`'s list in next_slot while the
 // first k-tiles land; every wave reads it after the prologue barrier (next,
 // have_next).
-// PRE (the AXPY, whose first k-tile otherwise waits behind the previous
-// tile's output stores): each wave loads its share of the next job's tile 0
-// into stage 0 (free since the barrier after tile nk - 2) once its last
-// k-step's MFMAs are issued (DmaCtx::pre), so that its latency overlaps
-// their drain and the epilogue, which stages in halves above stage 0;
-// pre_issued: this job's tile 0 was loaded so. In GRAM and POLY the extra
-// staging barriers cost more than the shorter first wait saves.
+// PRE: each wave loads its share of the next job's tile 0 into stage 0 (free
+// since the barrier after tile nk - 2) once its last k-step's MFMAs are
+// issued (DmaCtx::pre), so that the load overlaps their drain and the
+// epilogue (which stages above stage 0) instead of queueing behind the
+// epilogue's stores; pre_issued: this job's tile 0 was loaded so.
 template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD, bool PRE>
 __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem, int xcd,
                                          int next_local, int* next_slot, bool pre_issued, TileJob& next,
@@ -1415,7 +1329,9 @@ ns_gemm_dma(const NsArgs args) {
   __builtin_amdgcn_s_setprio(1);
   const int x = (int)(blockIdx.x & 7);
   const int P = (int)(gridDim.x >> 3);
-  constexpr bool PRE = QT;
+  // the next job's tile 0 early: AXPY and GRAM (POLY, with it, would need
+  // more registers than leave room for the AdamW update beside it)
+  constexpr bool PRE = QT || EPI == EPI_GRAM;
   TileJob J;
   int local = (int)(blockIdx.x >> 3);
   bool have = map_job_at(args, x, local, J);
