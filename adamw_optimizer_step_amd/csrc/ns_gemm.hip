@@ -727,9 +727,10 @@ struct DmaCtx {
   // the block's next job, whose k-tile 0 this wave loads into stage 0 after
   // its last k-tile (pre): its source, as src / q_step / lane_off
   bool pre;
+  bool n_trans;             // the next job's tile 0 in the transposed (two-row) layout
   const uint16_t* n_src;
   int64_t n_q_step;
-  int n_lane_off[2];
+  int n_ld;                 // its row pitch: the lane offsets are computed at the issue
 };
 
 // k-step KKI of k-tile kt: its MFMAs run on the fragments in (fa, fb) while
@@ -954,6 +955,8 @@ __device__ __forceinline__ void dma_next_src(const NsArgs& args, const TileJob& 
   const bool isP = wave < NW / 2;
   const int ld = isP ? G.ldP : G.ldQ;
   c.pre = true;
+  c.n_ld = ld;
+  c.n_trans = QT && (!isP || (G.p_upper && J.bi > 0));
   if (QT && (!isP || (G.p_upper && J.bi > 0))) {
     // rows k 0..63 of Q^T (Q waves) or of B's stored upper triangle (P waves
     // left of the diagonal block), two 512-byte rows per instruction
@@ -963,17 +966,26 @@ __device__ __forceinline__ void dma_next_src(const NsArgs& args, const TileJob& 
                                      (int64_t)((wave - NW / 2) * 16) * ld + (int64_t)J.bj * BN;
     c.n_src = base;
     c.n_q_step = 2 * (int64_t)ld;
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      c.n_lane_off[par] = (lane >> 5) * ld + (((lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3))) << 3);
   } else {
     c.n_src = reinterpret_cast<const uint16_t*>(isP ? G.P : G.Q) + (int64_t)J.mat * (isP ? G.sP : G.sQ) +
               (int64_t)((isP ? J.bi * BM : J.bj * BN) + (wave % (NW / 2)) * Gd::PANEL) * ld;
     c.n_q_step = (int64_t)RPI * ld;
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      c.n_lane_off[par] = (lane / CPR) * ld + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
   }
+}
+
+// Issue this wave's share of the next job's tile 0 into stage 0 (see
+// dma_next_src), the lane offsets computed here from the lane and the pitch,
+// so that they are not held in registers through the main loop
+template <int DPW>
+__device__ __forceinline__ void dma_issue_next(const DmaCtx& c) {
+  using namespace dma;
+  const int lane = c.lane, ld = c.n_ld;
+  int lo[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    lo[par] = c.n_trans ? (lane >> 5) * ld + (((lane & 31) ^ (4 * ((2 * par + (lane >> 5)) & 3))) << 3)
+                        : (lane / CPR) * ld + (((lane % CPR) ^ swz(par * RPI + lane / CPR)) << 3);
+  dma_issue<DPW>(c.wave_fill, c.n_src, c.n_q_step, lo, 0);
 }
 
 // f(std::integral_constant<int, I>()) for I = B .. E-1, in order
@@ -1197,12 +1209,12 @@ __device__ __forceinline__ void dma_epilogue(const NsArgs& args, const NsGroup& 
 // Wave 0 stores job `next_local` of XCD `xcd`'s list in next_slot while the
 // first k-tiles land; every wave reads it after the prologue barrier (next,
 // have_next).
-// PRE: each wave loads its share of the next job's tile 0 into stage 0 (free
+// Each wave loads its share of the next job's tile 0 into stage 0 (free
 // since the barrier after tile nk - 2) once its last k-step's MFMAs are
 // issued (DmaCtx::pre), so that the load overlaps their drain and the
 // epilogue (which stages above stage 0) instead of queueing behind the
 // epilogue's stores; pre_issued: this job's tile 0 was loaded so.
-template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD, bool PRE>
+template <int EPI, bool FOLD, int WGM, int WGN, bool QT, bool UPD>
 __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, unsigned char* smem, int xcd,
                                          int next_local, int* next_slot, bool pre_issued, TileJob& next,
                                          bool& have_next) {
@@ -1239,7 +1251,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   // run.
 #pragma unroll
   for (int t = 0; t < STAGES; ++t) {
-    if (PRE && t == 0 && pre_issued) continue;
+    if (t == 0 && pre_issued) continue;
     if (QT && t < c.dma_t_end)
       dma_issue<DPW>(c.wave_fill + t * STAGE_BYTES, c.src_t, c.q_step_t, c.lane_off_t, (int64_t)t * c.k_step_t);
     else
@@ -1263,16 +1275,16 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   have_next = next.gi >= 0;
   c.n_src = c.src;
   c.n_q_step = c.q_step;
-  c.n_lane_off[0] = c.lane_off[0];
-  c.n_lane_off[1] = c.lane_off[1];
-  if (PRE && have_next) dma_next_src<WGM, WGN, QT>(args, next, wave, lane, c);
+  c.n_ld = 0;
+  c.n_trans = false;
+  if (have_next) dma_next_src<WGM, WGN, QT>(args, next, wave, lane, c);
   // a diagonal tile of a symmetric product: the waves whose blocks all lie
   // below the diagonal (rows 128..255, columns 0..127) compute nothing
   const bool mirror_lower = !QT && G.symmetric && J.bi == J.bj;
   if (mirror_lower && c.wm * Gd::WTM >= BM / 2 && (c.wn + 1) * Gd::WTN <= BN / 2) {
     static_assert(QT || BM == BN, "square tiles");
     dma_skip_ktiles<WGM, WGN>(c);
-    if (PRE && c.pre) dma_issue<DPW>(c.wave_fill, c.n_src, c.n_q_step, c.n_lane_off, 0);
+    if (c.pre) dma_issue_next<DPW>(c);
     lds_barrier();   // as the other waves' barrier before their epilogue
     return;
   }
@@ -1303,7 +1315,7 @@ __device__ __forceinline__ void dma_tile(const NsArgs& args, const TileJob& J, u
   for (; kt < c.nk; ++kt) dma_ktile<-1, WGM, WGN, QT>(c, kt, acc, f0a, f0b, f1a, f1b);
   // stage 0 last held tile nk - 2 (nk is a multiple of 4), which every wave
   // had read before the barrier at the end of that tile
-  if (PRE && c.pre) dma_issue<DPW>(c.wave_fill, c.n_src, c.n_q_step, c.n_lane_off, 0);
+  if (c.pre) dma_issue_next<DPW>(c);
   lds_barrier();   // every wave has read the last k-tile (stage 1, reused by the staging)
   dma_epilogue<EPI, WGM, WGN, FOLD, UPD>(args, G, J, acc, smem, tid, mirror_lower, false, sc);
 }
@@ -1329,9 +1341,6 @@ ns_gemm_dma(const NsArgs args) {
   __builtin_amdgcn_s_setprio(1);
   const int x = (int)(blockIdx.x & 7);
   const int P = (int)(gridDim.x >> 3);
-  // the next job's tile 0 early: AXPY and GRAM (POLY, with it, would need
-  // more registers than leave room for the AdamW update beside it)
-  constexpr bool PRE = QT || EPI == EPI_GRAM;
   TileJob J;
   int local = (int)(blockIdx.x >> 3);
   bool have = map_job_at(args, x, local, J);
@@ -1342,14 +1351,14 @@ ns_gemm_dma(const NsArgs args) {
     int* const slot = slots + 4 * ((j + 1) & 1);
     TileJob N;
     bool more;
-    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD, PRE>(args, J, smem, x, local + P, slot, pre, N, more);
+    dma_tile<EPI, FOLD, WGM, WGN, QT, UPD>(args, J, smem, x, local + P, slot, pre, N, more);
     // every wave has read the staged output before the next job's DMA lands
-    // over it (with PRE its tile 0, in stage 0, is already in flight)
+    // over it (its tile 0, in stage 0, is already in flight)
     lds_barrier();
     local += P;
     J = N;
     have = more;
-    pre = PRE && more;
+    pre = more;
   }
 }
 
