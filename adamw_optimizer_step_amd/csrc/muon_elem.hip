@@ -1,9 +1,11 @@
 // Muon elementwise and reduction kernels (gfx950), HBM-bound.
 //
-//   k_rowsumsq_momentum  per row of the Nesterov look-ahead Mt = G + beta*m1,
-//                        m1 = beta*M + G: sum of squares (a wave per 4 rows,
-//                        up to 16 16-byte loads per lane in flight, butterfly
-//                        shuffle reduction; no atomics)
+//   k_rowsumsq_rows      per row of the Nesterov look-ahead Mt = G + beta*m1,
+//                        m1 = beta*M + G: sum of squares (a wave per row of at
+//                        most 4096 columns, all of a lane's 16-byte loads in
+//                        flight, butterfly shuffle reduction; no atomics)
+//   k_rowsumsq_momentum  the same for longer or unaligned rows (a wave per 4
+//                        rows, up to 16 16-byte loads per lane in flight)
 //   k_finalize           per matrix: Frobenius scale, MuonEq row factors,
 //                        NorMuon row factors
 //   k_pre                momentum update M <- m1 (stored), X0 = Mt * f_row,
@@ -99,8 +101,8 @@ __global__ void __launch_bounds__(256) k_rowsumsq_momentum(const ElemArgs a) {
           const int r = row0 + rr + u / CPB, c = (c0 + u % CPB) * 512 + lane * 8;
           ok[u] = r < a.R && c < a.C;
           const int64_t off = ok[u] ? (int64_t)r * a.C + c : 0;
-          raw_load<DTG>(eptr<DTG>(gp, off), g[u]);
-          raw_load<DTM>(eptr<DTM>(mp, off), m[u]);
+          raw_load<DTG, kNT>(eptr<DTG>(gp, off), g[u]);
+          raw_load<DTM, kNT>(eptr<DTM>(mp, off), m[u]);
         }
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
@@ -138,6 +140,49 @@ __global__ void __launch_bounds__(256) k_rowsumsq_momentum(const ElemArgs a) {
   }
 }
 
+// One wave per row, four rows per block, rows of at most 512 CH columns
+// (vector path): a lane's CH chunks of G and of M are loaded together, then
+// summed in the order k_rowsumsq_momentum uses (its chunks in column order,
+// then the butterfly), so both give the same bits. Many small blocks keep the
+// loads of the whole launch in flight with no tail of half-empty waves. The
+// loads are non-temporal: k_pre reads G and M again only after the other
+// groups' passes have streamed through the caches, so keeping them there
+// gains nothing and delays the write-back of what the previous pass wrote.
+template <int DTG, int DTM, int CH>
+__global__ void __launch_bounds__(256) k_rowsumsq_rows(const ElemArgs a) {
+  const int bpm = (a.R + 3) >> 2;
+  const int k = blockIdx.x / bpm;
+  const int r = (blockIdx.x - k * bpm) * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= a.R) return;
+  const void* gp = a.mat[k].g;
+  const void* mp = a.mat[k].m;
+  Raw8<DTG> g[CH];
+  Raw8<DTM> m[CH];
+  bool ok[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int c = u * 512 + lane * 8;
+    ok[u] = c < a.C;
+    const int64_t off = ok[u] ? (int64_t)r * a.C + c : 0;
+    raw_load<DTG, kNT>(eptr<DTG>(gp, off), g[u]);
+    raw_load<DTM, kNT>(eptr<DTM>(mp, off), m[u]);
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float m1, mt;
+      momentum1(raw_at<DTG>(g[u], e), raw_at<DTM>(m[u], e), a.beta, a.nesterov, m1, mt);
+      const float t = __builtin_fmaf(mt, mt, acc);
+      acc = ok[u] ? t : acc;
+    }
+  }
+  const float n2 = wave_sum(acc);
+  if (lane == 0) a.rowsq[(int64_t)k * a.row_stride + r] = n2;
+}
+
 // Row sums of squares of a workspace buffer in the parameter's layout (the
 // update U, for MuonEq POST).
 template <int DTX>
@@ -164,9 +209,15 @@ __global__ void __launch_bounds__(256) k_rowsumsq_buffer(const ElemArgs a) {
   }
 }
 
+// Row values are read kFinBatch per thread at a time, every load issued before
+// the first use, so a matrix of R rows costs R / (256 kFinBatch) memory
+// round trips per pass instead of R / 256 dependent ones.
+constexpr int kFinBatch = 16;
+
 // One block per matrix, every group of the launch (a group's matrices are
-// blocks g.block_begin ..); fixed-order reduction (strided partial sums, then
-// an LDS tree), so results do not depend on scheduling.
+// blocks g.block_begin ..); fixed-order reduction (thread t sums rows t,
+// t + 256, ... in that order, then an LDS tree), so results do not depend on
+// scheduling or on the batching of the loads.
 __global__ void __launch_bounds__(256) k_finalize(const FinalizeArgs fa) {
   __shared__ float red[256];
   int gi = 0;
@@ -178,14 +229,21 @@ __global__ void __launch_bounds__(256) k_finalize(const FinalizeArgs fa) {
   const int t = threadIdx.x;
   const int mode = a.mode;
   float part = 0.0f;
-  for (int i = t; i < a.R; i += 256) {
-    const float q = rs[i];
-    if (mode == 1 || mode == 4) {
-      const float n = sqrtf(q);
-      const float y = n / (n + fa.eq_eps);   // norm of the equilibrated row
-      part += y * y;
-    } else {
-      part += q;
+#pragma unroll 1
+  for (int i0 = t; i0 < a.R; i0 += 256 * kFinBatch) {
+    float q[kFinBatch];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) q[j] = rs[min(i0 + 256 * j, a.R - 1)];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) {
+      if (i0 + 256 * j >= a.R) break;
+      if (mode == 1 || mode == 4) {
+        const float n = sqrtf(q[j]);
+        const float y = n / (n + fa.eq_eps);   // norm of the equilibrated row
+        part += y * y;
+      } else {
+        part += q[j];
+      }
     }
   }
   red[t] = part;
@@ -204,20 +262,28 @@ __global__ void __launch_bounds__(256) k_finalize(const FinalizeArgs fa) {
   if (mode == 0) {
     const float s = 1.0f / (sqrtf(total) + fa.norm_eps);
     for (int i = t; i < a.R; i += 256) rf[i] = s;
-  } else if (mode == 1) {
-    const float s = 1.0f / (sqrtf(total) + fa.norm_eps);
-    for (int i = t; i < a.R; i += 256) rf[i] = s / (sqrtf(rs[i]) + fa.eq_eps);
   } else if (mode == 4) {
     // MuonEq pre with the row factors already applied (k_pre_rows): only the
     // matrix's Frobenius factor, in the row-factor slot of row 0
     if (t == 0) rf[0] = 1.0f / (sqrtf(total) + fa.norm_eps);
-  } else if (mode == 2) {
-    const float rho = sqrtf(total) / sqrtf((float)a.R);
-    for (int i = t; i < a.R; i += 256) rf[i] = rho / (sqrtf(rs[i]) + fa.eq_eps);
   } else {
-    // row RMS: ||U_i|| / sqrt(cols)
+    // per-row factors from the row sums: mode 1 s / (||row|| + eq_eps), mode 2
+    // rho / (||row|| + eq_eps), mode 3 (row RMS) 1 / (||row|| / sqrt(C) + eq_eps)
+    const float num = mode == 1 ? 1.0f / (sqrtf(total) + fa.norm_eps)
+                    : mode == 2 ? sqrtf(total) / sqrtf((float)a.R) : 1.0f;
     const float sc = sqrtf((float)a.C);
-    for (int i = t; i < a.R; i += 256) rf[i] = 1.0f / (sqrtf(rs[i]) / sc + fa.eq_eps);
+#pragma unroll 1
+    for (int i0 = t; i0 < a.R; i0 += 256 * kFinBatch) {
+      float q[kFinBatch];
+#pragma unroll
+      for (int j = 0; j < kFinBatch; ++j) q[j] = rs[min(i0 + 256 * j, a.R - 1)];
+#pragma unroll
+      for (int j = 0; j < kFinBatch; ++j) {
+        const int i = i0 + 256 * j;
+        if (i >= a.R) break;
+        rf[i] = mode == 3 ? 1.0f / (sqrtf(q[j]) / sc + fa.eq_eps) : num / (sqrtf(q[j]) + fa.eq_eps);
+      }
+    }
   }
 }
 
@@ -552,14 +618,22 @@ __global__ void __launch_bounds__(256) k_bf16_round(const float* in, uint16_t* o
   } while (0)
 
 hipError_t launch_rowsumsq_momentum(int dt_g, int dt_m, const ElemArgs& a, hipStream_t s) {
+  // chunks of 512 columns per row
+  const int cpr = (a.C + 511) / 512;
+  if (a.vec && a.C <= kPreRowsMaxCols) {
+    const int blocks = a.count * ((a.R + 3) / 4);
+    if (blocks <= 0) return hipSuccess;
+    if (cpr <= 1) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_rows, 1, dim3(blocks), dim3(256), 0, s, a);
+    else if (cpr <= 2) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_rows, 2, dim3(blocks), dim3(256), 0, s, a);
+    else if (cpr <= 4) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_rows, 4, dim3(blocks), dim3(256), 0, s, a);
+    else MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_rows, 8, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  // longer rows (eight-chunk batches) or unaligned ones (scalar loads): four
+  // rows per wave
   const int blocks = a.count * ((a.R + kRowsPerBlock - 1) / kRowsPerBlock);
   if (blocks <= 0) return hipSuccess;
-  // chunks of 512 columns per row, rounded up to the kernel's batch width
-  const int cpr = (a.C + 511) / 512;
-  if (cpr <= 1) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 1, dim3(blocks), dim3(256), 0, s, a);
-  else if (cpr <= 2) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 2, dim3(blocks), dim3(256), 0, s, a);
-  else if (cpr <= 4) MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 4, dim3(blocks), dim3(256), 0, s, a);
-  else MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 8, dim3(blocks), dim3(256), 0, s, a);
+  MA_DISPATCH2C(dt_g, dt_m, k_rowsumsq_momentum, 8, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -276,12 +276,12 @@ def test_ragged_groups(eq, cautious, wd, dts):
                                  ("bf16", "f32", "f32")])
 def test_row_norms_of_long_rows(steps, dts):
     """MuonEq row factors for rows of one to seventeen 512-column chunks:
-    1024 columns (two chunks, four rows read together), 1536 (three of a
-    four-chunk batch), 4608 and 8200 (eight-chunk batches, the last partial),
-    row counts that leave a wave's four rows part empty, and a tall matrix
-    whose rows are 1000 long. With no Newton-Schulz step the update is the
-    row-scaled look-ahead itself, so a row sum that lost a chunk shows at the
-    fp32 tolerance."""
+    1024 and 1536 columns (a wave per row, two and three of four chunk
+    slots), 4608 and 8200 (four rows per wave in eight-chunk batches, the
+    last partial), row counts that leave a block's four rows part empty, and a
+    tall matrix whose rows are 1000 long (the second chunk partial). With no
+    Newton-Schulz step the update is the row-scaled look-ahead itself, so a
+    row sum that lost a chunk shows at the fp32 tolerance."""
     rng = np.random.default_rng(91)
     groups_np = []
     for R, C, n in [(20, 1024, 2), (7, 1536, 1), (5, 4608, 1), (3, 8200, 1), (1100, 1000, 1)]:
