@@ -8,7 +8,7 @@
 //                        rows, up to 16 16-byte loads per lane in flight)
 //   k_finalize           per matrix: Frobenius scale, MuonEq row factors,
 //                        NorMuon row factors
-//   k_pre                momentum update M <- m1 (stored), X0 = Mt * f_row,
+//   k_pre, k_pre_t       momentum update M <- m1 (stored), X0 = Mt * f_row,
 //                        written in the parameter's layout and transposed
 //                        (through an LDS tile) into the Newton-Schulz buffers
 //   k_post               cautious decoupled decay and the update, W <- W'
@@ -374,6 +374,83 @@ __global__ void __launch_bounds__(256) k_pre(const ElemArgs a) {
   }
 }
 
+// The transposed-only form of k_pre (vector path, no copy in the
+// parameter's layout): tiles of 64 rows x kPreTileCols columns, so that each
+// row of G and M is read and M written in runs of 2 kPreTileCols bytes
+// rather than 128. Thread t covers columns 8 (t % (kPreTileCols / 8)) .. +7
+// of every (256 / (kPreTileCols / 8))-th row, all of its loads issued before
+// the first use; X0^T is written 16 bytes per thread from the LDS tile, rows
+// of X0^T beyond the 64-column tiles of the extent left alone. Same
+// arithmetic and the same stored values as k_pre.
+constexpr int kPreTileCols = 128;
+
+template <int DTG, int DTM, int DTX>
+__global__ void __launch_bounds__(256) k_pre_t(const ElemArgs a, const int tiles_cw) {
+  constexpr int TC = kPreTileCols;
+  constexpr int TPR = TC / 8;      // threads per tile row
+  constexpr int RPP = 256 / TPR;   // tile rows per pass
+  constexpr int NP = 64 / RPP;     // passes
+  __shared__ float tile[64][TC + 1];
+  const int tiles = a.tiles_r * tiles_cw;
+  const int k = blockIdx.x / tiles;
+  const int t = blockIdx.x - k * tiles;
+  const int tr = t / tiles_cw, tc = t - tr * tiles_cw;
+  const int r0 = tr * 64, c0 = tc * TC;
+  const void* gp = a.mat[k].g;
+  void* mp = a.mat[k].m;
+  const int tid = threadIdx.x;
+  const int cl = (tid % TPR) * 8;
+  const int c = c0 + cl;
+  Raw8<DTG> g[NP];
+  Raw8<DTM> m[NP];
+  bool ok[NP];
+#pragma unroll
+  for (int h = 0; h < NP; ++h) {
+    const int r = r0 + tid / TPR + RPP * h;
+    ok[h] = r < a.R && c < a.C;
+    const int64_t off = ok[h] ? (int64_t)r * a.C + c : 0;
+    raw_load<DTG, kNT>(eptr<DTG>(gp, off), g[h]);
+    raw_load<DTM, kNT>(eptr<DTM>(static_cast<const void*>(mp), off), m[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < NP; ++h) {
+    const int rl = tid / TPR + RPP * h;
+    const int r = r0 + rl;
+    float x[8];
+    if (ok[h]) {
+      const float f = a.rowf ? a.rowf[(int64_t)k * a.row_stride + r] : 1.0f;
+      float m1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float mt;
+        momentum1(raw_at<DTG>(g[h], e), raw_at<DTM>(m[h], e), a.beta, a.nesterov, m1[e], mt);
+        x[e] = __fmul_rn(mt, f);
+      }
+      store8<DTM, kNT>(eptr<DTM>(mp, (int64_t)r * a.C + c), m1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[rl][cl + e] = x[e];
+  }
+  __syncthreads();
+  // row (c0 + cc) of xt holds column cc of the tile
+  void* xt = eptr<DTX>(a.xt, (int64_t)k * a.x_stride);
+  const int rows_t = a.tiles_c * 64;
+#pragma unroll
+  for (int h = 0; h < TC / 32; ++h) {
+    const int cc = (tid >> 3) + 32 * h;
+    const int rr = (tid & 7) * 8;
+    if (c0 + cc < rows_t) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = tile[rr + e][cc];
+      store8<DTX>(eptr<DTX>(xt, (int64_t)(c0 + cc) * a.ld_t + r0 + rr), y);
+    }
+  }
+}
+
 // One wave per row of a matrix with no more rows than columns (its
 // iteration layout is the parameter's): M <- m1, the row's sum of squares of
 // Mt (summed in the order k_rowsumsq_momentum uses) and the X0 row
@@ -685,7 +762,27 @@ static void launch_pre_x(int dt_g, int dt_m, const ElemArgs& a, int blocks, hipS
   else hipLaunchKernelGGL((k_pre<DT_F32, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a);
 }
 
+template <int DTX>
+static void launch_pre_t_x(int dt_g, int dt_m, const ElemArgs& a, int blocks, int tiles_cw, hipStream_t s) {
+  if (dt_g == DT_BF16 && dt_m == DT_BF16)
+    hipLaunchKernelGGL((k_pre_t<DT_BF16, DT_BF16, DTX>), dim3(blocks), dim3(256), 0, s, a, tiles_cw);
+  else if (dt_g == DT_BF16) hipLaunchKernelGGL((k_pre_t<DT_BF16, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a, tiles_cw);
+  else if (dt_m == DT_BF16) hipLaunchKernelGGL((k_pre_t<DT_F32, DT_BF16, DTX>), dim3(blocks), dim3(256), 0, s, a, tiles_cw);
+  else hipLaunchKernelGGL((k_pre_t<DT_F32, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a, tiles_cw);
+}
+
 hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s) {
+  if (a.xt && !a.xd && a.vec && !a.pure_copy) {
+    // the transposed copy alone: wide tiles (the 64-column tiles of the
+    // extent, kPreTileCols / 64 to a tile, the last one part empty)
+    const int per = kPreTileCols / 64;
+    const int tiles_cw = (a.tiles_c + per - 1) / per;
+    const int blocks = a.count * a.tiles_r * tiles_cw;
+    if (blocks <= 0) return hipSuccess;
+    if (dt_x == DT_BF16) launch_pre_t_x<DT_BF16>(dt_g, dt_m, a, blocks, tiles_cw, s);
+    else launch_pre_t_x<DT_F32>(dt_g, dt_m, a, blocks, tiles_cw, s);
+    return hipGetLastError();
+  }
   const int blocks = a.count * a.tiles_r * a.tiles_c;
   if (blocks <= 0) return hipSuccess;
   if (dt_x == DT_BF16) launch_pre_x<DT_BF16>(dt_g, dt_m, a, blocks, s);
