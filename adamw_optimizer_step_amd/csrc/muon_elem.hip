@@ -8,9 +8,12 @@
 //                        rows, up to 16 16-byte loads per lane in flight)
 //   k_finalize           per matrix: Frobenius scale, MuonEq row factors,
 //                        NorMuon row factors
-//   k_pre, k_pre_t       momentum update M <- m1 (stored), X0 = Mt * f_row,
+//   k_pre                momentum update M <- m1 (stored), X0 = Mt * f_row,
 //                        written in the parameter's layout and transposed
-//                        (through an LDS tile) into the Newton-Schulz buffers
+//                        (through an LDS tile) into the Newton-Schulz buffers;
+//                        k_pre_t (transposed copy only, wider tiles) and
+//                        k_pre_d (parameter's layout only, no tile) are its
+//                        one-copy forms
 //   k_post               cautious decoupled decay and the update, W <- W'
 //
 // Sources: momentum and look-ahead -- "Chapter 4: The MuonAdamW Optimizer",
@@ -451,6 +454,61 @@ __global__ void __launch_bounds__(256) k_pre_t(const ElemArgs a, const int tiles
   }
 }
 
+// The direct-only form of k_pre (vector path, no transposed copy): nothing
+// is transposed, so no tile either. Thread i of the launch covers 16-byte
+// chunks i, i + stride, ... of the matrix's extent r_ext x c_ext in row-major
+// order (whole rows of chunks are read and written in one run), kPreDirectCh
+// chunks per thread, every load issued before the first use. Chunks outside
+// R x C are stored as zeros (the iteration buffer's padding). Same arithmetic
+// and the same stored values as k_pre.
+constexpr int kPreDirectCh = 4;
+
+template <int DTG, int DTM, int DTX>
+__global__ void __launch_bounds__(256) k_pre_d(const ElemArgs a, const int bpm) {
+  const int k = blockIdx.x / bpm;
+  const int b = blockIdx.x - k * bpm;
+  const int cpr = a.c_ext >> 3;                       // chunks per extent row
+  const int64_t nch = (int64_t)a.r_ext * cpr;
+  const void* gp = a.mat[k].g;
+  void* mp = a.mat[k].m;
+  void* xd = eptr<DTX>(a.xd, (int64_t)k * a.x_stride);
+  Raw8<DTG> g[kPreDirectCh];
+  Raw8<DTM> m[kPreDirectCh];
+  bool ok[kPreDirectCh];
+  int rr[kPreDirectCh], cc[kPreDirectCh];
+#pragma unroll
+  for (int u = 0; u < kPreDirectCh; ++u) {
+    const int64_t i = ((int64_t)b * kPreDirectCh + u) * 256 + threadIdx.x;
+    const bool in = i < nch;
+    rr[u] = in ? (int)(i / cpr) : a.r_ext;
+    cc[u] = in ? (int)(i - (int64_t)rr[u] * cpr) * 8 : 0;
+    ok[u] = rr[u] < a.R && cc[u] < a.C;
+    const int64_t off = ok[u] ? (int64_t)rr[u] * a.C + cc[u] : 0;
+    raw_load<DTG, kNT>(eptr<DTG>(gp, off), g[u]);
+    raw_load<DTM, kNT>(eptr<DTM>(static_cast<const void*>(mp), off), m[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kPreDirectCh; ++u) {
+    if (rr[u] >= a.r_ext) continue;
+    float x[8];
+    if (ok[u]) {
+      const float f = a.rowf ? a.rowf[(int64_t)k * a.row_stride + rr[u]] : 1.0f;
+      float m1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float mt;
+        momentum1(raw_at<DTG>(g[u], e), raw_at<DTM>(m[u], e), a.beta, a.nesterov, m1[e], mt);
+        x[e] = __fmul_rn(mt, f);
+      }
+      store8<DTM, kNT>(eptr<DTM>(mp, (int64_t)rr[u] * a.C + cc[u]), m1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    }
+    store8<DTX>(eptr<DTX>(xd, (int64_t)rr[u] * a.ld_d + cc[u]), x);
+  }
+}
+
 // One wave per row of a matrix with no more rows than columns (its
 // iteration layout is the parameter's): M <- m1, the row's sum of squares of
 // Mt (summed in the order k_rowsumsq_momentum uses) and the X0 row
@@ -771,6 +829,15 @@ static void launch_pre_t_x(int dt_g, int dt_m, const ElemArgs& a, int blocks, in
   else hipLaunchKernelGGL((k_pre_t<DT_F32, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a, tiles_cw);
 }
 
+template <int DTX>
+static void launch_pre_d_x(int dt_g, int dt_m, const ElemArgs& a, int blocks, int bpm, hipStream_t s) {
+  if (dt_g == DT_BF16 && dt_m == DT_BF16)
+    hipLaunchKernelGGL((k_pre_d<DT_BF16, DT_BF16, DTX>), dim3(blocks), dim3(256), 0, s, a, bpm);
+  else if (dt_g == DT_BF16) hipLaunchKernelGGL((k_pre_d<DT_BF16, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a, bpm);
+  else if (dt_m == DT_BF16) hipLaunchKernelGGL((k_pre_d<DT_F32, DT_BF16, DTX>), dim3(blocks), dim3(256), 0, s, a, bpm);
+  else hipLaunchKernelGGL((k_pre_d<DT_F32, DT_F32, DTX>), dim3(blocks), dim3(256), 0, s, a, bpm);
+}
+
 hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream_t s) {
   if (a.xt && !a.xd && a.vec && !a.pure_copy) {
     // the transposed copy alone: wide tiles (the 64-column tiles of the
@@ -781,6 +848,16 @@ hipError_t launch_pre(int dt_g, int dt_m, int dt_x, const ElemArgs& a, hipStream
     if (blocks <= 0) return hipSuccess;
     if (dt_x == DT_BF16) launch_pre_t_x<DT_BF16>(dt_g, dt_m, a, blocks, tiles_cw, s);
     else launch_pre_t_x<DT_F32>(dt_g, dt_m, a, blocks, tiles_cw, s);
+    return hipGetLastError();
+  }
+  if (a.xd && !a.xt && a.vec && !a.pure_copy && (a.ld_d & 7) == 0 && (a.c_ext & 7) == 0 && a.c_ext <= a.ld_d) {
+    // the direct copy alone: row-major runs, no tile
+    const int64_t nch = (int64_t)a.r_ext * (a.c_ext >> 3);
+    const int bpm = (int)((nch + 256 * kPreDirectCh - 1) / (256 * kPreDirectCh));
+    const int blocks = a.count * bpm;
+    if (blocks <= 0) return hipSuccess;
+    if (dt_x == DT_BF16) launch_pre_d_x<DT_BF16>(dt_g, dt_m, a, blocks, bpm, s);
+    else launch_pre_d_x<DT_F32>(dt_g, dt_m, a, blocks, bpm, s);
     return hipGetLastError();
   }
   const int blocks = a.count * a.tiles_r * a.tiles_c;
