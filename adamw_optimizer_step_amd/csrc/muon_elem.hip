@@ -148,9 +148,11 @@ __global__ void __launch_bounds__(256) k_rowsumsq_momentum(const ElemArgs a) {
 // summed in the order k_rowsumsq_momentum uses (its chunks in column order,
 // then the butterfly), so both give the same bits. Many small blocks keep the
 // loads of the whole launch in flight with no tail of half-empty waves. The
-// loads are non-temporal: k_pre reads G and M again only after the other
-// groups' passes have streamed through the caches, so keeping them there
-// gains nothing and delays the write-back of what the previous pass wrote.
+// loads are non-temporal. The group's second read of G and M (k_pre_t or
+// k_pre) comes after the factors of every group are known, so when other
+// groups take their one-pass form in between, their traffic has evicted these
+// lines anyway; allocating them would only push out the previous pass's
+// dirty lines earlier, in the middle of this read.
 template <int DTG, int DTM, int CH>
 __global__ void __launch_bounds__(256) k_rowsumsq_rows(const ElemArgs a) {
   const int bpm = (a.R + 3) >> 2;
