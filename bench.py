@@ -105,7 +105,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs the optimizer step on one GPU; "
+        print(json.dumps({"error": "the benchmark runs the optimizer step on one GPU; "
                                    f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported"}))
         sys.exit(2)
 

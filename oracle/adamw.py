@@ -6,8 +6,8 @@ bias corrections folded into the step size and the denominator, then
 addcdiv), and "Chapter 4: The MuonAdamW Optimizer", section "The AdamW Step"
 (same rule, moments written as lerp; the two forms agree in exact arithmetic).
 
-Precision contract (the reading this build fixes, since the pages give the rule
-in exact arithmetic only):
+Precision contract (the reading taken here, since the pages give the rule in
+exact arithmetic only):
 
 * scalars that depend on the hyperparameters and the step count are computed
   once in float64 and rounded to binary32:
